@@ -1,0 +1,291 @@
+"""Plain, slow CPU oracle for the DSA sparse-attention decode/prefill path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it.  It shares no code with the HIP library (no kernels,
+headers, helpers, tables or constants are common to the two); the storage
+format constants below are restated here from the format definition, not
+imported.
+
+Sources (the pages this follows):
+  * "Accelerating GLM-5.3-Flash on H200" (lmsys.org blog), section 1
+    "Architecture and workloads": DSA keeps historical KV and an indexer selects
+    the relevant positions.
+  * same page, section 3, "Larger KV tiles for DSA Partial": after the indexer
+    selects KV positions, Partial loads them and computes Q K^T, an online
+    softmax and the weighted value sum; KV splits produce intermediates that a
+    Combine step merges; Figure 4: an index width that is not a multiple of the
+    KV tile is covered by virtual padding, the physical index tensor unchanged.
+  * "A million-token context on 16 H200s" (vLLM news summary), Interpretation:
+    MLA's latent KV row is shared by all 64 heads.
+  * "GLM-5.3-Flash" SGLang cookbook, section 2 "Size both memory pools" and
+    "Extend the cache hierarchy": a paged KV pool plus a separate DSA indexer
+    pool; FP8 KV cache is the default on MI355X.
+
+The pages never write the formulas down.  Readings adopted where they are
+silent (each is listed with its reason in the design notes of the repository):
+  * indexer score  s[t,p] = sum_h w[t,h] * relu(q_I[t,h,:] . k_I[p,:])  over the
+    visible positions p <= pos_t, one 128-d key per position shared by the 16
+    indexer heads;
+  * top-k keeps the k highest scores, ties going to the lower position; the
+    result is returned in ascending position order and padded with -1;
+  * attention:  z_j = sm_scale * q[h] . K[i_j]  over all 576 dims,
+    o[h] = softmax(z) . K[i][:, :512],  lse[h] = log sum_j exp(z_j);
+  * split s of S covers index columns [s*c, min(W,(s+1)*c)) with
+    c = tile * ceil(ceil(W/tile)/S); an empty split yields (o=0, lse=-inf);
+  * combine:  lse = logsumexp_s lse_s,  o = sum_s exp(lse_s - lse) * o_s;
+  * FP8 rows: 576 OCP E4M3FN codes followed by nine little-endian fp32 scales,
+    one per 64 consecutive elements; value = decode(code) * scale.
+
+All floating point here is float64 (numpy).  Indexer scores are returned as
+float32 after an exact float64 computation (integer-valued inputs keep every
+partial sum an exact integer below 2**24, so any summation order agrees).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Storage format, restated from its definition (page = 64 token slots).
+# ---------------------------------------------------------------------------
+PAGE_TOKENS = 64
+HEADS = 64
+D_LATENT = 512
+D_ROPE = 64
+D_QK = D_LATENT + D_ROPE          # 576
+IDX_HEADS = 16
+IDX_DIM = 128
+
+KV_BF16 = 0
+KV_FP8 = 1
+
+FP8_GROUP = 64                    # one fp32 scale per 64 consecutive elements
+FP8_NGROUPS = D_QK // FP8_GROUP   # 9
+FP8_ROW_STRIDE = 640              # 576 codes + 36 scale bytes + 28 pad bytes
+FP8_SCALE_OFFSET = 576
+BF16_ROW_STRIDE = 2 * D_QK        # 1152
+KEY_ROW_BYTES = 2 * IDX_DIM       # 256
+
+
+def latent_row_stride(kv_dtype: int) -> int:
+    return FP8_ROW_STRIDE if kv_dtype == KV_FP8 else BF16_ROW_STRIDE
+
+
+def pool_plane_offsets(kv_dtype: int, num_pages: int) -> tuple[int, int, int]:
+    """(latent plane offset, index plane offset, total bytes) of a pool buffer.
+
+    The latent plane holds num_pages * 64 rows at the row stride; the indexer
+    key plane follows it, 64 rows of 256 bytes per page, at the same page id.
+    """
+    latent_bytes = num_pages * PAGE_TOKENS * latent_row_stride(kv_dtype)
+    index_bytes = num_pages * PAGE_TOKENS * KEY_ROW_BYTES
+    return 0, latent_bytes, latent_bytes + index_bytes
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+def e4m3fn_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3FN code: 1 sign, 4 exponent (bias 7), 3 mantissa
+    bits; exponent field 0 encodes subnormals m/8 * 2**-6; S.1111.111 is NaN and
+    there is no infinity (max finite 448)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3fn_table() -> np.ndarray:
+    return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+_E4M3 = e4m3fn_table()
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 is the upper half of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Pool addressing (paged KV pool + page table)
+# ---------------------------------------------------------------------------
+class PoolView:
+    """Host view of pool bytes: logical (request b, position p) -> page
+    page_table[b][p // 64], slot p % 64."""
+
+    def __init__(self, pool_bytes: np.ndarray, num_pages: int, kv_dtype: int):
+        self.buf = np.asarray(pool_bytes, dtype=np.uint8).reshape(-1)
+        self.num_pages = int(num_pages)
+        self.kv_dtype = int(kv_dtype)
+        self.stride = latent_row_stride(kv_dtype)
+        self.lat_off, self.idx_off, total = pool_plane_offsets(kv_dtype, num_pages)
+        assert self.buf.size >= total, (self.buf.size, total)
+
+    def _phys_rows(self, page_row: np.ndarray, positions: np.ndarray) -> np.ndarray:
+        positions = np.asarray(positions, dtype=np.int64)
+        pages = np.asarray(page_row, dtype=np.int64)[positions // PAGE_TOKENS]
+        assert np.all((pages >= 0) & (pages < self.num_pages))
+        return pages * PAGE_TOKENS + positions % PAGE_TOKENS
+
+    def latent_rows(self, page_row, positions) -> np.ndarray:
+        """Dequantized latent rows [n, 576] (float64)."""
+        phys = self._phys_rows(page_row, positions)
+        if phys.size == 0:
+            return np.zeros((0, D_QK))
+        starts = self.lat_off + phys * self.stride
+        raw = self.buf[starts[:, None] + np.arange(self.stride)[None, :]]
+        if self.kv_dtype == KV_BF16:
+            bits = raw[:, :2 * D_QK].copy().view(np.uint16)
+            return bf16_bits_to_f64(bits)
+        codes = raw[:, :D_QK]
+        scales = raw[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 4 * FP8_NGROUPS].copy()
+        scales = scales.view('<f4').astype(np.float64)            # [n, 9]
+        vals = _E4M3[codes]                                        # [n, 576]
+        group = np.arange(D_QK) // FP8_GROUP
+        return vals * scales[:, group]
+
+    def index_keys(self, page_row, positions) -> np.ndarray:
+        """Indexer keys [n, 128] (float64)."""
+        phys = self._phys_rows(page_row, positions)
+        if phys.size == 0:
+            return np.zeros((0, IDX_DIM))
+        starts = self.idx_off + phys * KEY_ROW_BYTES
+        raw = self.buf[starts[:, None] + np.arange(KEY_ROW_BYTES)[None, :]]
+        return bf16_bits_to_f64(raw.copy().view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Step 1: indexer scores
+# ---------------------------------------------------------------------------
+def index_scores(q_idx: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Scores of one query token against keys [n,128].
+
+    s[p] = sum_h w[h] * max(0, q_idx[h,:] . keys[p,:]); q_idx [16,128], w [16].
+    Computed in float64, returned as float32.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dots = np.asarray(keys, dtype=np.float64) @ q_idx.T          # [n, 16]
+    s = np.maximum(dots, 0.0) @ w                                 # [n]
+    return s.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: top-k
+# ---------------------------------------------------------------------------
+def topk_positions(scores: np.ndarray, k: int) -> np.ndarray:
+    """The k visible positions with the highest score, ties to the lower
+    position, returned ascending and padded with -1 to length k."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    pos = np.arange(n)
+    order = np.lexsort((pos, -scores))        # primary: score desc; then pos asc
+    keep = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:keep.size] = keep
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 3: attention over the selected rows, split-KV partials and combine
+# ---------------------------------------------------------------------------
+def attend(q: np.ndarray, rows: np.ndarray, sm_scale: float):
+    """Softmax attention of 64 heads over rows [m,576].
+
+    Returns (o [64,512], lse [64]); an empty row set gives (0, -inf)."""
+    q = np.asarray(q, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    if rows.shape[0] == 0:
+        return np.zeros((q.shape[0], D_LATENT)), np.full(q.shape[0], -np.inf)
+    z = sm_scale * (q @ rows.T)                                   # [64, m]
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    denom = e.sum(axis=1, keepdims=True)
+    p = e / denom
+    o = p @ rows[:, :D_LATENT]
+    lse = (zmax + np.log(denom))[:, 0]
+    return o, lse
+
+
+def num_iterations(width: int, tile: int) -> int:
+    """Loop iterations that cover an index width with KV tiles of `tile`."""
+    return -(-int(width) // int(tile))
+
+
+def virtual_columns(width: int, tile: int) -> int:
+    """Columns covered by the loop, the last tile's tail being virtual padding."""
+    return num_iterations(width, tile) * int(tile)
+
+
+def split_bounds(width: int, tile: int, splits: int):
+    """Contiguous, tile-aligned column ranges of the S splits."""
+    per = -(-num_iterations(width, tile) // int(splits))
+    c = per * int(tile)
+    return [(min(width, s * c), min(width, (s + 1) * c)) for s in range(int(splits))]
+
+
+def valid_mask(idx_cols: np.ndarray, pos: int) -> np.ndarray:
+    """Index entries outside [0, pos] (including the -1 padding) are masked."""
+    idx_cols = np.asarray(idx_cols, dtype=np.int64)
+    return (idx_cols >= 0) & (idx_cols <= pos)
+
+
+def partial(q, idx_row, pos, rows_of, sm_scale, tile, splits):
+    """Split-KV partials of one token: (o_part [S,64,512], lse_part [S,64]).
+
+    rows_of(positions) returns the dequantized latent rows of those positions.
+    """
+    o_parts = np.zeros((splits, q.shape[0], D_LATENT))
+    lse_parts = np.full((splits, q.shape[0]), -np.inf)
+    idx_row = np.asarray(idx_row, dtype=np.int64)
+    for s, (a, b) in enumerate(split_bounds(idx_row.shape[0], tile, splits)):
+        cols = idx_row[a:b]
+        cols = cols[valid_mask(cols, pos)]
+        o_parts[s], lse_parts[s] = attend(q, rows_of(cols), sm_scale)
+    return o_parts, lse_parts
+
+
+def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge split partials: lse = logsumexp_s lse_s, o = sum_s e^(lse_s-lse) o_s."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)                                     # [64]
+    finite = np.isfinite(m)
+    safe_m = np.where(finite, m, 0.0)
+    wts = np.where(np.isfinite(lse_parts), np.exp(lse_parts - safe_m[None, :]), 0.0)
+    tot = wts.sum(axis=0)
+    lse = np.where(finite, safe_m + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    o = np.einsum('sh,shd->hd', wts, o_parts)
+    o = np.where(finite[:, None], o / np.where(finite, tot, 1.0)[:, None], 0.0)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# The whole per-token path
+# ---------------------------------------------------------------------------
+def token_path(pool: PoolView, page_row, pos: int, q_idx, w, q, k: int,
+               sm_scale: float, tile: int = 64, splits: int = 1):
+    """Indexer -> top-k -> partial -> combine for one query token.
+
+    Returns dict(scores [pos+1] f32, idx [k] i32, o [64,512] f64, lse [64] f64).
+    """
+    visible = np.arange(pos + 1)
+    keys = pool.index_keys(page_row, visible)
+    scores = index_scores(q_idx, w, keys)
+    idx = topk_positions(scores, k)
+    o_p, lse_p = partial(np.asarray(q, np.float64), idx, pos,
+                         lambda cols: pool.latent_rows(page_row, cols),
+                         sm_scale, tile, splits)
+    o, lse = combine(o_p, lse_p)
+    return dict(scores=scores, idx=idx, o=o, lse=lse)
