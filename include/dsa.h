@@ -1,0 +1,225 @@
+/*
+ * dsa.h - C ABI of the DSA (DeepSeek-style sparse attention) hot path on
+ * AMD MI355X (gfx950).
+ *
+ * Per query token the path is: an indexer scores every visible cached
+ * position, a top-k keeps the best positions, 64 attention heads attend over
+ * only the selected rows of a shared MLA latent KV cache (split-KV partials),
+ * and a combine step merges the partials.  Sources:
+ *   [LMSYS-1] lmsys.org, "Accelerating GLM-5.3-Flash on H200", section 1
+ *             "Architecture and workloads" (DSA stores historical KV; an
+ *             indexer selects relevant positions).
+ *   [LMSYS-2] same page, section 2 "Turning cache capacity into concurrency",
+ *             "KV-only decode RadixCache" (prefix KV shared across requests;
+ *             Lp + N*Ls slots instead of N*(Lp+Ls)).
+ *   [LMSYS-3] same page, section 3, "Larger KV tiles for DSA Partial" and its
+ *             Figure 4 (Partial = gather selected KV, QK^T, online softmax,
+ *             weighted value sum; KV tile 32 or 128; index width not padded
+ *             physically; splits add intermediate writes merged by Combine;
+ *             dispatch from architecture, layout and query parallelism).
+ *   [VLLM]    "A million-token context on 16 H200s", Interpretation (MLA's
+ *             latent KV row is shared by all 64 heads).
+ *   [SGL]     SGLang cookbook "GLM-5.3-Flash", section 2 "Size both memory
+ *             pools", "Keep the KV and DSA backends paired", "Extend the cache
+ *             hierarchy" (paged KV pool, separate DSA indexer pool, FP8 KV on
+ *             MI355X, BF16 KV elsewhere).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - The caller owns all device memory (allocated with PyTorch or hipMalloc);
+ *     the library never allocates device memory and never synchronizes.
+ *   - Compute entry points only enqueue work on `stream` (a hipStream_t passed
+ *     as void*, NULL = the default stream); DSA_OK means "enqueued".
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     an error nothing is launched, the status is returned and a message is
+ *     kept for dsa_last_error() (thread-local).
+ *   - Model dimensions are fixed: 64 heads, latent 512 + rope 64 (q/k dim
+ *     576, v dim 512), indexer 16 heads x 128, 64-token pages.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+#define DSA_PAGE_TOKENS 64
+#define DSA_HEADS 64
+#define DSA_D_LATENT 512
+#define DSA_D_ROPE 64
+#define DSA_D_QK 576
+#define DSA_IDX_HEADS 16
+#define DSA_IDX_DIM 128
+
+typedef int32_t dsa_status;
+enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad enum */
+  DSA_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  DSA_ERR_NO_SPACE = 3,    /* pool exhausted (allocation is all-or-nothing) */
+  DSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  DSA_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+};
+
+/* KV element formats [SGL "Keep the KV and DSA backends paired"]. */
+enum {
+  DSA_KV_BF16 = 0,         /* 576 bf16 per row */
+  DSA_KV_FP8_E4M3_S64 = 1  /* 576 OCP E4M3FN codes + 9 fp32 scales (one per 64) */
+};
+
+int32_t dsa_abi_version(void);
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* dsa_last_error(void);
+const char* dsa_status_string(dsa_status s);
+
+/* ------------------------------------------------------------------------
+ * Paged KV pool [SGL "Size both memory pools"; LMSYS-2].
+ *
+ * One caller-owned device buffer holds two planes addressed by the same page
+ * id: the latent plane (num_pages * 64 rows at latent_row_stride bytes) and,
+ * after it, the indexer-key plane (num_pages * 64 rows of 128 bf16).
+ * Latent row formats:
+ *   BF16: 576 bf16 (1152 bytes), stride 1152.
+ *   FP8 : bytes [0,576) E4M3FN codes, [576,612) nine little-endian fp32
+ *         scales (element c has value decode(code[c]) * scale[c/64]),
+ *         [612,640) padding; stride 640 (five 128-byte lines).
+ * Logical position p of request b lives at page page_table[b][p/64], slot
+ * p%64.  Page contents are written by the caller through this layout.
+ * ------------------------------------------------------------------------ */
+typedef struct dsa_pool_layout {
+  int32_t page_tokens;        /* 64 */
+  int32_t kv_dtype;
+  int32_t d_latent, d_rope, d_index;     /* 512, 64, 128 */
+  int32_t latent_row_bytes;   /* algorithmic bytes per row: 612 (FP8) or 1152 */
+  int32_t latent_row_stride;  /* 640 (FP8) or 1152 */
+  int32_t scale_offset;       /* 576 for FP8, -1 for BF16 */
+  int32_t index_row_bytes;    /* 256 */
+  int32_t reserved;
+  int64_t latent_plane_offset;  /* 0 */
+  int64_t index_plane_offset;   /* num_pages * 64 * latent_row_stride */
+  int64_t total_bytes;          /* bytes the pool buffer must hold */
+} dsa_pool_layout;
+
+/* Host-only.  Fills *out (host) for num_pages pages of kv_dtype. */
+dsa_status dsa_pool_layout_query(int32_t kv_dtype, int32_t num_pages, dsa_pool_layout* out);
+
+typedef struct dsa_pool dsa_pool; /* opaque host object owned by the library */
+
+/* Host-only.  Wraps the caller's device buffer `dev_base` (256-byte aligned,
+ * at least total_bytes long) as a pool of num_pages pages, all free.
+ * *out receives a handle to release with dsa_pool_destroy. */
+dsa_status dsa_pool_create(void* dev_base, int64_t bytes, int32_t num_pages,
+                           int32_t kv_dtype, dsa_pool** out);
+void dsa_pool_destroy(dsa_pool* pool);
+/* Host-only page bookkeeping [LMSYS-2 prefix sharing]:
+ *   alloc   - take n free pages (refcount 1), ids written to host array ids;
+ *             all-or-nothing: DSA_ERR_NO_SPACE leaves the pool unchanged.
+ *   share   - refcount++ of n live pages (a request reusing prefix pages).
+ *   release - refcount-- of n live pages; a page returns to the free list at 0.
+ *             Releasing a free page is DSA_ERR_INVALID_ARG and changes nothing. */
+dsa_status dsa_pool_alloc(dsa_pool* pool, int32_t n, int32_t* ids /* host out */);
+dsa_status dsa_pool_share(dsa_pool* pool, const int32_t* ids /* host */, int32_t n);
+dsa_status dsa_pool_release(dsa_pool* pool, const int32_t* ids /* host */, int32_t n);
+int32_t dsa_pool_free_pages(const dsa_pool* pool);
+int32_t dsa_pool_refcount(const dsa_pool* pool, int32_t page_id); /* -1 if out of range */
+int32_t dsa_pool_num_pages(const dsa_pool* pool);
+int32_t dsa_pool_kv_dtype(const dsa_pool* pool);
+
+/* ------------------------------------------------------------------------
+ * Batch description shared by the compute calls.
+ *   num_reqs requests; request b owns query tokens [q_offsets[b],
+ *   q_offsets[b+1]) (q_offsets: device int32[num_reqs+1], nondecreasing,
+ *   q_offsets[0] = 0, q_offsets[num_reqs] = num_tokens).
+ *   tok_pos: device int32[num_tokens], the absolute position of each query
+ *   token; it sees positions [0, tok_pos[t]] of its request (causal, itself
+ *   included).
+ *   page_table: device int32[num_reqs * pt_stride]; entry [b][j] is the page of
+ *   logical page j of request b; entries past ceil((tok_pos+1)/64) are never
+ *   read.
+ *   max_q: host bound on tokens per request; max_ctx: host bound on
+ *   tok_pos[t] + 1 (both size the launch grid; tokens beyond them are not
+ *   processed).
+ * ------------------------------------------------------------------------ */
+
+/* Indexer scores [LMSYS-1; VLLM: "the indexer is not partitioned"]:
+ *   scores[t*ld + p] = sum_{h<16} w[t*16+h] * max(0, q_idx[t,h,:] . key(p))
+ * for p in [0, min(tok_pos[t], max_ctx-1)]; entries past that are not written.
+ * q_idx: bf16 [num_tokens,16,128]; w: fp32 [num_tokens,16]; key(p) is the
+ * 128-d bf16 indexer key of position p of the token's request.  Products are
+ * accumulated in fp32 (never rounded through bf16): integer-valued inputs
+ * whose partial sums stay below 2^24 give exact results.
+ * ld >= max_ctx, ld % 4 == 0; scores 16-byte aligned. */
+dsa_status dsa_index_scores(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                            const int32_t* q_offsets, int32_t num_reqs, int32_t max_q,
+                            const int32_t* tok_pos, int32_t num_tokens, int32_t max_ctx,
+                            const uint16_t* q_idx, const float* w, float* scores, int64_t ld,
+                            void* stream);
+
+/* Top-k over each token's visible scores [LMSYS-1 indexer selection; the
+ * blog's "top-k v2" change]: the k positions with the highest score among
+ * [0, min(tok_pos[t], max_ctx-1)], ties going to the lower position, written
+ * to idx[t*k ..] in ascending position order and padded with -1 when fewer
+ * than k positions are visible.  Scores are compared as fp32 (NaN unsupported).
+ * Rows longer than 65,536 positions use `workspace` (device, 256-byte
+ * aligned) of at least dsa_topk_workspace_bytes() bytes; 0 bytes otherwise.
+ * Limits: 1 <= k <= 16384; max_ctx <= 65536 * (65536 / k). */
+size_t dsa_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t k);
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos, int32_t num_tokens,
+                    int32_t max_ctx, int32_t k, int32_t* idx, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Dispatch plan of the Partial step [LMSYS-3 and Figure 4].  Host-only.
+ *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose.
+ *   num_splits: KV splits per token, or 0 = choose from query parallelism
+ *   (num_tokens) and cu_count (0 = 256, MI355X).
+ * Output (host): tile, splits, iters_total = ceil(width/tile), iters_per_split
+ * = ceil(iters_total/splits), cols_per_split = tile*iters_per_split,
+ * virtual_cols = tile*iters_total, padding_cols = virtual_cols - width.
+ * Split s covers index columns [s*cols_per_split, min(width,(s+1)*cols_per_split)). */
+typedef struct dsa_partial_plan {
+  int32_t tile, splits, iters_total, iters_per_split;
+  int32_t cols_per_split, virtual_cols, padding_cols, reserved;
+} dsa_partial_plan;
+dsa_status dsa_plan_partial(int32_t num_tokens, int32_t width, int32_t kv_tile,
+                            int32_t num_splits, int32_t cu_count, dsa_partial_plan* out);
+
+/* Sparse MLA Partial [LMSYS-3; VLLM head sharing].  For token t, split s and
+ * head h, over the valid columns j of split s:
+ *   z_j = sm_scale * q[t,h,:] . K(idx[t*width + j])        (576-d)
+ *   o_part[t,s,h,:] = sum_j softmax(z)_j * K(idx[..j])[0:512]   (normalized)
+ *   lse_part[t,s,h] = ln sum_j exp(z_j)
+ * K(p) is the dequantized latent row of position p of the token's request.
+ * An index entry is valid when 0 <= idx <= tok_pos[t]; others (including -1
+ * padding) are skipped, repeats count each time.  The index tensor is
+ * consumed as is: width need not be a multiple of the tile (the loop's last
+ * tile is padded virtually).  A split with no valid column yields o = 0,
+ * lse = -inf.  kv_tile and num_splits must be the resolved values of a plan
+ * (kv_tile in {32, 64, 128}; num_splits >= 1).
+ * q: bf16 [num_tokens,64,576]; idx: int32 [num_tokens,width];
+ * o_part: fp32 [num_tokens,num_splits,64,512]; lse_part: fp32
+ * [num_tokens,num_splits,64].  All 16-byte aligned. */
+dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t* page_table,
+                                  int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                                  const int32_t* tok_pos, int32_t num_tokens, const uint16_t* q,
+                                  const int32_t* idx, int32_t width, float sm_scale,
+                                  int32_t kv_tile, int32_t num_splits, float* o_part,
+                                  float* lse_part, void* stream);
+
+/* Combine [LMSYS-3]: per token and head,
+ *   lse = ln sum_s exp(lse_part_s),  out = sum_s exp(lse_part_s - lse) * o_part_s
+ * with splits whose lse is -inf contributing nothing (all -inf: out = 0,
+ * lse = -inf).  out: bf16 [num_tokens,64,512] (round to nearest even);
+ * lse: fp32 [num_tokens,64]. */
+dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,
+                       int32_t num_splits, uint16_t* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

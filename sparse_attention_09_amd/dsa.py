@@ -1,0 +1,348 @@
+"""Python binding of libdsa.so (ctypes): argument marshalling only.
+
+Every compute call passes tensor data pointers and the current HIP stream to
+the C ABI declared in include/dsa.h; all arithmetic runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.  If the library is not
+built, importing this module works but every call raises: there is no CPU
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+KV_BF16 = 0
+KV_FP8 = 1
+PAGE_TOKENS = 64
+HEADS = 64
+D_LATENT = 512
+D_QK = 576
+IDX_HEADS = 16
+IDX_DIM = 128
+
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_NO_SPACE",
+          4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_HIP"}
+
+# Every symbol include/dsa.h declares (checked by the CPU tests).
+EXPORTS = [
+    "dsa_abi_version", "dsa_last_error", "dsa_status_string",
+    "dsa_pool_layout_query", "dsa_pool_create", "dsa_pool_destroy", "dsa_pool_alloc",
+    "dsa_pool_share", "dsa_pool_release", "dsa_pool_free_pages", "dsa_pool_refcount",
+    "dsa_pool_num_pages", "dsa_pool_kv_dtype",
+    "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
+    "dsa_sparse_mla_partial", "dsa_combine",
+]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class PoolLayout(ctypes.Structure):
+    _fields_ = [("page_tokens", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_index", ctypes.c_int32), ("latent_row_bytes", ctypes.c_int32),
+                ("latent_row_stride", ctypes.c_int32), ("scale_offset", ctypes.c_int32),
+                ("index_row_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("latent_plane_offset", ctypes.c_int64), ("index_plane_offset", ctypes.c_int64),
+                ("total_bytes", ctypes.c_int64)]
+
+
+class PartialPlan(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("iters_total", ctypes.c_int32), ("iters_per_split", ctypes.c_int32),
+                ("cols_per_split", ctypes.c_int32), ("virtual_cols", ctypes.c_int32),
+                ("padding_cols", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_09_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        sz = ctypes.c_size_t
+        sig = {
+            "dsa_abi_version": (i32, []),
+            "dsa_last_error": (ctypes.c_char_p, []),
+            "dsa_status_string": (ctypes.c_char_p, [i32]),
+            "dsa_pool_layout_query": (i32, [i32, i32, ctypes.POINTER(PoolLayout)]),
+            "dsa_pool_create": (i32, [vp, i64, i32, i32, ctypes.POINTER(vp)]),
+            "dsa_pool_destroy": (None, [vp]),
+            "dsa_pool_alloc": (i32, [vp, i32, vp]),
+            "dsa_pool_share": (i32, [vp, vp, i32]),
+            "dsa_pool_release": (i32, [vp, vp, i32]),
+            "dsa_pool_free_pages": (i32, [vp]),
+            "dsa_pool_refcount": (i32, [vp, i32]),
+            "dsa_pool_num_pages": (i32, [vp]),
+            "dsa_pool_kv_dtype": (i32, [vp]),
+            "dsa_index_scores": (i32, [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, vp, i64, vp]),
+            "dsa_topk_workspace_bytes": (sz, [i32, i32, i32]),
+            "dsa_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "dsa_plan_partial": (i32, [i32, i32, i32, i32, i32, ctypes.POINTER(PartialPlan)]),
+            "dsa_sparse_mla_partial": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32,
+                                             i32, vp, vp, vp]),
+            "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DsaError(status, lib().dsa_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().dsa_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# --------------------------------------------------------------------------- pool
+def pool_layout(kv_dtype: int, num_pages: int) -> PoolLayout:
+    out = PoolLayout()
+    _check(lib().dsa_pool_layout_query(kv_dtype, num_pages, ctypes.byref(out)))
+    return out
+
+
+class Pool:
+    """A paged KV pool over a caller-owned uint8 device tensor."""
+
+    def __init__(self, buffer: torch.Tensor, num_pages: int, kv_dtype: int):
+        _need(buffer, "buffer", torch.uint8)
+        self.buffer = buffer
+        self.num_pages = int(num_pages)
+        self.kv_dtype = int(kv_dtype)
+        self.layout = pool_layout(kv_dtype, num_pages)
+        h = ctypes.c_void_p()
+        _check(lib().dsa_pool_create(ctypes.c_void_p(buffer.data_ptr()), buffer.numel(), num_pages,
+                                     kv_dtype, ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def device(self) -> torch.device:
+        return self.buffer.device
+
+    def close(self):
+        if self._h:
+            lib().dsa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> list:
+        ids = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().dsa_pool_alloc(self._h, n, ids))
+        return list(ids[:n])
+
+    def share(self, ids) -> None:
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(lib().dsa_pool_share(self._h, arr, len(ids)))
+
+    def release(self, ids) -> None:
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(lib().dsa_pool_release(self._h, arr, len(ids)))
+
+    def free_pages(self) -> int:
+        return lib().dsa_pool_free_pages(self._h)
+
+    def refcount(self, page_id: int) -> int:
+        return lib().dsa_pool_refcount(self._h, page_id)
+
+
+# --------------------------------------------------------------------------- path
+def plan_partial(num_tokens: int, width: int, kv_tile: int = 0, num_splits: int = 0,
+                 cu_count: int = 0) -> PartialPlan:
+    out = PartialPlan()
+    _check(lib().dsa_plan_partial(num_tokens, width, kv_tile, num_splits, cu_count,
+                                  ctypes.byref(out)))
+    return out
+
+
+def topk_workspace_bytes(num_tokens: int, max_ctx: int, k: int) -> int:
+    return int(lib().dsa_topk_workspace_bytes(num_tokens, max_ctx, k))
+
+
+def index_scores(pool: Pool, page_table, q_offsets, tok_pos, q_idx, w, max_q: int, max_ctx: int,
+                 scores: Optional[torch.Tensor] = None, ld: Optional[int] = None) -> torch.Tensor:
+    dev = pool.device
+    T = tok_pos.numel()
+    B = q_offsets.numel() - 1
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(q_idx, "q_idx", torch.bfloat16, dev, (T, IDX_HEADS, IDX_DIM))
+    _need(w, "w", torch.float32, dev, (T, IDX_HEADS))
+    if ld is None:
+        ld = (max(max_ctx, 1) + 3) // 4 * 4
+    if scores is None:
+        scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    _need(scores, "scores", torch.float32, dev)
+    if scores.dim() != 2 or scores.shape[0] != T or scores.shape[1] != ld:
+        raise ValueError("scores must be [num_tokens, ld]")
+    _check(lib().dsa_index_scores(pool.handle, _ptr(page_table), page_table.shape[-1], _ptr(q_offsets),
+                                  B, max_q, _ptr(tok_pos), T, max_ctx, _ptr(q_idx), _ptr(w),
+                                  _ptr(scores), ld, _stream(dev)))
+    return scores
+
+
+def topk(scores: torch.Tensor, tok_pos: torch.Tensor, k: int, max_ctx: int,
+         idx: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    T, ld = scores.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, dev, (T, k))
+    need = topk_workspace_bytes(T, max_ctx, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib().dsa_topk(_ptr(scores), ld, _ptr(tok_pos), T, max_ctx, k, _ptr(idx),
+                          _ptr(workspace), ws_bytes, _stream(dev)))
+    return idx
+
+
+def sparse_mla_partial(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_scale: float,
+                       kv_tile: int, num_splits: int, o_part=None, lse_part=None):
+    dev = pool.device
+    T = tok_pos.numel()
+    B = q_offsets.numel() - 1
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(q, "q", torch.bfloat16, dev, (T, HEADS, D_QK))
+    _need(idx, "idx", torch.int32, dev)
+    width = idx.shape[-1]
+    if o_part is None:
+        o_part = torch.empty((T, num_splits, HEADS, D_LATENT), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((T, num_splits, HEADS), dtype=torch.float32, device=dev)
+    _need(o_part, "o_part", torch.float32, dev, (T, num_splits, HEADS, D_LATENT))
+    _need(lse_part, "lse_part", torch.float32, dev, (T, num_splits, HEADS))
+    _check(lib().dsa_sparse_mla_partial(pool.handle, _ptr(page_table), page_table.shape[-1],
+                                        _ptr(q_offsets), B, _ptr(tok_pos), T, _ptr(q), _ptr(idx),
+                                        width, float(sm_scale), kv_tile, num_splits, _ptr(o_part),
+                                        _ptr(lse_part), _stream(dev)))
+    return o_part, lse_part
+
+
+def combine(o_part: torch.Tensor, lse_part: torch.Tensor, out=None, lse=None):
+    dev = o_part.device
+    _need(o_part, "o_part", torch.float32, dev)
+    _need(lse_part, "lse_part", torch.float32, dev)
+    T, S = o_part.shape[0], o_part.shape[1]
+    if out is None:
+        out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (T, HEADS, D_LATENT))
+    _need(lse, "lse", torch.float32, dev, (T, HEADS))
+    _check(lib().dsa_combine(_ptr(o_part), _ptr(lse_part), T, S, _ptr(out), _ptr(lse),
+                             _stream(dev)))
+    return out, lse
+
+
+def default_sm_scale() -> float:
+    return 1.0 / math.sqrt(D_QK)
+
+
+class DsaPath:
+    """The four calls of one decode/prefill step, with their buffers allocated
+    once for a fixed batch shape (so repeated steps allocate nothing)."""
+
+    def __init__(self, pool: Pool, page_table, q_offsets, tok_pos, max_q: int, max_ctx: int,
+                 k: int, kv_tile: int = 0, num_splits: int = 0, sm_scale: Optional[float] = None,
+                 cu_count: int = 0):
+        self.pool = pool
+        self.page_table, self.q_offsets, self.tok_pos = page_table, q_offsets, tok_pos
+        self.max_q, self.max_ctx, self.k = int(max_q), int(max_ctx), int(k)
+        self.sm_scale = default_sm_scale() if sm_scale is None else float(sm_scale)
+        T = tok_pos.numel()
+        self.T = T
+        self.plan = plan_partial(T, k, kv_tile, num_splits, cu_count)
+        dev = pool.device
+        self.ld = (max(max_ctx, 1) + 3) // 4 * 4
+        self.scores = torch.empty((T, self.ld), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        need = topk_workspace_bytes(T, max_ctx, k)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+        S = self.plan.splits
+        self.o_part = torch.empty((T, S, HEADS, D_LATENT), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((T, S, HEADS), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+
+    def index_scores(self, q_idx, w):
+        return index_scores(self.pool, self.page_table, self.q_offsets, self.tok_pos, q_idx, w,
+                            self.max_q, self.max_ctx, self.scores, self.ld)
+
+    def topk(self):
+        return topk(self.scores, self.tok_pos, self.k, self.max_ctx, self.idx, self.workspace)
+
+    def partial(self, q):
+        return sparse_mla_partial(self.pool, self.page_table, self.q_offsets, self.tok_pos, q,
+                                  self.idx, self.sm_scale, self.plan.tile, self.plan.splits,
+                                  self.o_part, self.lse_part)
+
+    def combine(self):
+        return combine(self.o_part, self.lse_part, self.out, self.lse)
+
+    def step(self, q_idx, w, q):
+        self.index_scores(q_idx, w)
+        self.topk()
+        self.partial(q)
+        return self.combine()
