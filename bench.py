@@ -1,0 +1,209 @@
+"""Benchmark of the DSA sparse-attention path on one MI355X.
+
+One step = the whole path over one batch: indexer scores -> top-k -> sparse
+MLA partial -> combine, with inputs resident in HBM.  Default workload: the
+speculative-verify decode batch, 128 requests x 8 query tokens, 64K context
+each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
+64 heads.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+METRIC = "sparse-MLA query tokens/s + HBM GB/s % peak, 64K ctx top-2048, 64 heads"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
+
+
+def algorithmic_bytes(spec, plan, kv_row_bytes):
+    """Bytes each kernel must move at minimum, per launch (one step)."""
+    T = spec.num_tokens
+    k = spec.k
+    S = plan.splits
+    keys = 0
+    for L, q in zip(spec.ctx_lens, spec.q_per_req):
+        # a request's visible keys are read once for all its query tokens
+        keys += L * 256
+    vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
+              for p in range(L - q, L))
+    return {
+        # keys + indexer queries/weights + visible score writes
+        "index_scores": keys + T * (16 * 128 * 2 + 16 * 4) + vis * 4,
+        # visible score reads + index writes
+        "topk": vis * 4 + T * k * 4,
+        # index reads + selected latent rows + q + split partials
+        "partial": T * k * 4 + T * k * kv_row_bytes + T * 64 * 576 * 2 + T * S * 64 * (512 + 1) * 4,
+        # split partials in, bf16 output + lse out
+        "combine": T * S * 64 * (512 + 1) * 4 + T * 64 * (512 * 2 + 4),
+    }
+
+
+def flops(spec):
+    T, k = spec.num_tokens, spec.k
+    vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
+              for p in range(L - q, L))
+    return {"index_scores": vis * 16 * 128 * 2, "partial": T * 64 * k * (576 + 512) * 2}
+
+
+def cpu_baseline(wl, budget_s=12.0, max_tokens=64):
+    """The oracle, as written, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dsa_oracle as O
+    from tests._harness import HostView
+
+    s = wl.spec
+    tok_req = wl.tok_req.cpu().numpy()
+    order = list(range(s.num_tokens))
+    # sample whole requests from the front of the batch
+    reqs = sorted(set(int(tok_req[t]) for t in order[:max_tokens]))
+    hv = HostView(wl, reqs=reqs)
+    done = 0
+    t0 = time.perf_counter()
+    for t in order[:max_tokens]:
+        hv.token(t, 64, 1)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": done / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} query tokens of {s.name} (requests {reqs[0]}..{reqs[-1]}), "
+                      f"full per-token path (indexer over the whole context, top-k, attention, "
+                      f"combine) in float64 numpy; {dt:.1f} s",
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="verify_fp8_64k")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from sparse_attention_09_amd import dsa, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = synth.spec(args.workload)
+    print(f"[bench] generating {spec.name} seed={args.seed}", file=sys.stderr, flush=True)
+    wl = synth.generate(spec, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    pool = dsa.Pool(wl.pool, wl.num_pages, spec.kv_dtype)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx, spec.k,
+                       kv_tile=args.tile, num_splits=args.splits, sm_scale=spec.sm_scale,
+                       cu_count=cus)
+    plan = path.plan
+    print(f"[bench] plan tile={plan.tile} splits={plan.splits} cus={cus}", file=sys.stderr, flush=True)
+
+    def step():
+        path.step(wl.q_idx, wl.w, wl.q)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-path timing
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel timing on the same stream (separate loop, events between calls)
+    names = ["index_scores", "topk", "partial", "combine"]
+    calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk, lambda: path.partial(wl.q),
+             path.combine]
+    acc = {n: 0.0 for n in names}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs[0].record(stream)
+        for i, c in enumerate(calls):
+            c()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += evs[i].elapsed_time(evs[i + 1])
+    per_us = {n: 1000.0 * acc[n] / args.steps for n in names}
+
+    lay = dsa.pool_layout(spec.kv_dtype, 1)
+    byts = algorithmic_bytes(spec, plan, lay.latent_row_bytes)
+    fl = flops(spec)
+    kernels = {}
+    for n in names:
+        d = {"avg_us": round(per_us[n], 3), "alg_bytes": int(byts[n]),
+             "gbps": round(byts[n] / (per_us[n] * 1e-6) / 1e9, 1)}
+        if n in fl:
+            d["tflops"] = round(fl[n] / (per_us[n] * 1e-6) / 1e12, 2)
+        kernels[n] = d
+    dom = max(names, key=lambda n: per_us[n])
+    path_bytes = sum(byts.values())
+    path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
+    T = spec.num_tokens
+    value = T / (ms_step * 1e-3)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(kernels[dom]["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+            "alg_bytes_per_launch": int(byts[dom]), "avg_us": kernels[dom]["avg_us"]}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": spec.num_reqs, "query_tokens": T,
+                   "context": int(max(spec.ctx_lens)), "top_k": spec.k, "heads": 64,
+                   "kv": "fp8_e4m3_s64" if spec.kv_dtype == dsa.KV_FP8 else "bf16",
+                   "kv_tile": plan.tile, "splits": plan.splits},
+        "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
+                "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

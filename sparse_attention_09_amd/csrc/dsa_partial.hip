@@ -8,20 +8,30 @@
 // MLA's latent row is shared by all 64 heads, so one row read from HBM serves
 // 64 heads - which makes QK^T and PV dense enough for the matrix cores.
 //
-// One workgroup = one (token, split), 4 waves, wave w owns heads 16w..16w+15.
-// Per KV tile of TILE rows:
-//   * the selected rows are gathered through the page table with coalesced
-//     loads (each wave instruction reads 512 contiguous bytes of one row), FP8
-//     codes are dequantized in registers (exact E4M3->fp32, times the row's
-//     per-64 scale, rounded to bf16) and written to LDS twice: row-major K
-//     (576 wide, QK^T operand) and transposed V (512 x TILE, PV operand);
+// One workgroup = one (token, split).  Per KV tile of TILE rows:
+//   * the selected rows are gathered through the page table in (row, 64-column
+//     group) units: four 16-byte code loads plus one scale load per unit; FP8
+//     codes are dequantized in registers (exact E4M3 -> fp32, times the group
+//     scale, rounded to bf16) and written once to LDS as a row-major K tile
+//     (576 wide, swizzled against bank conflicts);
 //   * the next tile's rows are prefetched into registers while the current
-//     tile is computed;
-//   * S^T = K Q^T and O += P V run on the 16x16x32 bf16 MFMA with fp32
-//     accumulation; Q stays in registers for the whole split, the softmax
-//     state (running max and sum, log2 domain) in registers per head, and
-//     P goes from the S^T accumulators to the PV operand without leaving
-//     registers.
+//     tile is computed (gather loads are unconditional so nothing waits on them
+//     before the tile's stores);
+//   * S^T = K Q^T runs on the 16x16x32 bf16 MFMA with Q held in registers for
+//     the whole split; O += P V takes P straight from the S^T accumulators and
+//     reads V = K[:, :512] from the same LDS tile with the gfx950 transpose read
+//     (ds_read_b64_tr_b16), so no transposed copy is made;
+//   * the softmax keeps a per-head reference max in the log2 domain and only
+//     rescales O when a head's max grows by more than 2^8 (P stays <= 256, and
+//     the final normalisation is unaffected), so O is rarely touched.
+// Two layouts of the same scheme:
+//   * tiles of 32 and 64 rows: 8 waves, 2 per SIMD so the hardware interleaves
+//     LDS latency with MFMA work.  Waves w and w+4 own heads 16(w%4)..+16; each
+//     contracts one half of the 576 dims for S^T (half the Q registers) and the
+//     pair adds the two halves through LDS; both then run the same softmax and
+//     each accumulates one half of the 512 output columns;
+//   * tiles of 128 rows (the K tile alone takes 148 KB of LDS): 4 waves, wave
+//     w owns heads 16w..+16 for all dims and columns.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,10 +46,45 @@ using dsa::f32x4;
 using dsa::u32x2;
 using dsa::u32x4;
 
-constexpr int kThreads = 256;
-constexpr int kKStride = DSA_D_QK + 8;   // LDS row stride of K in bf16 (pad against bank conflicts)
+constexpr int kKStride = DSA_D_QK + 16;  // LDS row stride of the K tile in bf16 (296 dwords)
 constexpr int kRowChunk = 2048;          // index columns whose row addresses are resolved at once
 constexpr float kNegInf = -INFINITY;
+constexpr float kRescaleThreshold = 8.f; // log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS offset (bf16 units) of 16-byte chunk `chunk` of K-tile row r.  With a
+// 296-dword stride and the chunk index XOR-ed with ((r>>2)^(r>>3))&1, the
+// tile's three access patterns avoid bank conflicts: 16-byte stores by lanes
+// on 8 consecutive rows, 16-byte MFMA-operand reads by lanes on 16 consecutive
+// rows, and 8-byte transpose reads of 4 rows x 32 contiguous bytes.
+__device__ __forceinline__ int k_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__device__ __forceinline__ int k_chunk_off(int r, int chunk) {
+  return r * kKStride + ((chunk ^ k_swz(r)) << 3);
+}
+// The swizzle only flips bit 0 of the chunk index, so for an even chunk e:
+// chunk e of row r sits at r*stride + 8e + 8*swz(r), chunk e+1 at
+// r*stride + 8e + 8*(1-swz(r)).  Every access below is written as a per-lane
+// base plus compile-time offsets, which keeps address registers out of the
+// tile loop.
+
+// Transposed 4x16-bit read: lane i of each 16-lane group receives element i%4
+// of the 8-byte chunks addressed by lanes 4j + i/4 of its group, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Staging units.  V unit u covers row v_row(u), latent columns 64*v_grp(u) ..+64;
+// rope unit u covers row r_row(u), rope columns 16*r_piece(u) ..+16.  Eight
+// consecutive lanes take eight consecutive rows, so their stores spread over
+// the banks.
+__device__ __forceinline__ int v_row(int u) { return (u & 7) | ((u >> 6) << 3); }
+__device__ __forceinline__ int v_grp(int u) { return (u >> 3) & 7; }
+__device__ __forceinline__ int r_row(int u) { return (u & 7) | ((u >> 5) << 3); }
+__device__ __forceinline__ int r_piece(int u) { return (u >> 3) & 3; }
 
 struct PartialArgs {
   const uint8_t* latent;
@@ -59,208 +104,423 @@ struct PartialArgs {
   float* lse_part;
 };
 
-template <int TILE>
-struct TileSmem {
-  uint16_t k[TILE * kKStride];
-  uint16_t vt[DSA_D_LATENT * TILE];
-  int32_t rows[kRowChunk];
-};
-
-// XOR swizzle of the 8-row chunks inside one transposed-V row (column d), so
-// that both the transposed writes (consecutive lanes -> d, d+8, ...) and the
-// MFMA operand reads (consecutive lanes -> d, d+1, ...) spread over the banks.
-template <int TILE>
-__device__ __forceinline__ int vt_swizzle(int d) {
-  return (d ^ (d >> 3)) & (TILE / 8 - 1);
-}
-
-// Register staging of one tile's rows for one thread.
-template <int KV, int TILE>
+// Register staging of NR rows of a tile, spread over NT threads.
+template <int KV, int NR, int NT>
 struct Stage;
 
 // FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.
-template <int TILE>
-struct Stage<DSA_KV_FP8_E4M3_S64, TILE> {
+template <int NR, int NT>
+struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
   static constexpr int kStride = 640;
-  static constexpr int kVU = TILE / 32;                 // V units (8 rows x 8 cols) per thread
-  static constexpr int kRU = (TILE * 4 + kThreads - 1) / kThreads;  // rope units (1 row x 16 cols)
-  u32x2 vcode[kVU][8];
-  float vscale[kVU][8];
+  static constexpr int kVU = (NR * 8 + NT - 1) / NT;
+  static constexpr int kRU = (NR * 4 + NT - 1) / NT;
+  u32x4 vcode[kVU][4];
+  float vscale[kVU];
   u32x4 rcode[kRU];
   float rscale[kRU];
+  uint32_t vok, rok;   // bit i: unit i holds a valid row
 
+  // Unconditional loads: invalid rows read row 0 and are zeroed when stored.
   __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int tid) {
-    const int lane = tid & 63, wave = tid >> 6;
+    vok = rok = 0;
 #pragma unroll
     for (int i = 0; i < kVU; ++i) {
-      const int rg = wave + 4 * i;
+      const int u = tid + NT * i;
+      const int phys = u < NR * 8 ? rows[v_row(u)] : -1;
+      vok |= uint32_t(phys >= 0) << i;
+      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int phys = rows[8 * rg + e];
-        if (phys >= 0) {
-          const uint8_t* row = latent + int64_t(phys) * kStride;
-          vcode[i][e] = *reinterpret_cast<const u32x2*>(row + 8 * lane);
-          vscale[i][e] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * (lane >> 3));
-        } else {
-          vcode[i][e] = u32x2{0, 0};
-          vscale[i][e] = 0.f;
-        }
+      for (int m = 0; m < 4; ++m)
+        vcode[i][m] = *reinterpret_cast<const u32x4*>(row + 64 * v_grp(u) + 16 * m);
+      vscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * v_grp(u));
+    }
+#pragma unroll
+    for (int i = 0; i < kRU; ++i) {
+      const int u = tid + NT * i;
+      const int phys = u < NR * 4 ? rows[r_row(u)] : -1;
+      rok |= uint32_t(phys >= 0) << i;
+      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
+      rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * r_piece(u));
+      rscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+    }
+  }
+
+  // 16 codes -> 16 bf16 = chunks `chunk` (even), `chunk`+1 of row r
+  __device__ __forceinline__ static void put16(uint16_t* k, int r, int chunk, const u32x4& codes,
+                                               float scale) {
+    uint32_t b[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float f[4];
+      dsa::fp8x4_to_f32(codes[h], f);
+      b[2 * h] = dsa::pack_bf16x2(f[0] * scale, f[1] * scale);
+      b[2 * h + 1] = dsa::pack_bf16x2(f[2] * scale, f[3] * scale);
+    }
+    uint16_t* row = k + r * kKStride + 8 * chunk;
+    const int sw = k_swz(r);
+    *reinterpret_cast<u32x4*>(row + 8 * sw) = u32x4{b[0], b[1], b[2], b[3]};
+    *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = u32x4{b[4], b[5], b[6], b[7]};
+  }
+
+  // rows are stored at r0 + (unit row)
+  __device__ __forceinline__ void store(uint16_t* k, int r0, int tid) const {
+    const u32x4 z = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kVU; ++i) {
+      const int u = tid + NT * i;
+      const bool ok = (vok >> i) & 1u;
+      if (u < NR * 8) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          put16(k, r0 + v_row(u), 8 * v_grp(u) + 2 * m, ok ? vcode[i][m] : z, ok ? vscale[i] : 0.f);
       }
     }
 #pragma unroll
     for (int i = 0; i < kRU; ++i) {
-      const int u = tid + kThreads * i;
-      rcode[i] = u32x4{0, 0, 0, 0};
-      rscale[i] = 0.f;
-      if (u < TILE * 4) {
-        const int phys = rows[u >> 2];
-        if (phys >= 0) {
-          const uint8_t* row = latent + int64_t(phys) * kStride;
-          rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (u & 3));
-          rscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
-        }
-      }
-    }
-  }
-
-  // bf16 pairs of the 8 rows of V unit i: bits[e][m] holds cols 2m, 2m+1 of row e
-  __device__ __forceinline__ void vbits(int i, uint32_t bits[8][4]) const {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float f[8];
-      dsa::fp8x4_to_f32(vcode[i][e][0], f);
-      dsa::fp8x4_to_f32(vcode[i][e][1], f + 4);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        bits[e][m] = dsa::pack_bf16x2(f[2 * m] * vscale[i][e], f[2 * m + 1] * vscale[i][e]);
-    }
-  }
-  __device__ __forceinline__ void rbits(int i, uint32_t bits[8]) const {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float f[4];
-      dsa::fp8x4_to_f32(rcode[i][h], f);
-      bits[2 * h] = dsa::pack_bf16x2(f[0] * rscale[i], f[1] * rscale[i]);
-      bits[2 * h + 1] = dsa::pack_bf16x2(f[2] * rscale[i], f[3] * rscale[i]);
+      const int u = tid + NT * i;
+      const bool ok = (rok >> i) & 1u;
+      if (u < NR * 4)
+        put16(k, r0 + r_row(u), DSA_D_LATENT / 8 + 2 * r_piece(u), ok ? rcode[i] : z,
+              ok ? rscale[i] : 0.f);
     }
   }
 };
 
 // BF16 rows: 576 bf16, stride 1152.
-template <int TILE>
-struct Stage<DSA_KV_BF16, TILE> {
+template <int NR, int NT>
+struct Stage<DSA_KV_BF16, NR, NT> {
   static constexpr int kStride = 2 * DSA_D_QK;
-  static constexpr int kVU = TILE / 32;
-  static constexpr int kRU = (TILE * 4 + kThreads - 1) / kThreads;
+  static constexpr int kVU = (NR * 8 + NT - 1) / NT;
+  static constexpr int kRU = (NR * 4 + NT - 1) / NT;
   u32x4 vraw[kVU][8];
   u32x4 rraw[kRU][2];
+  uint32_t vok, rok;
 
   __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int tid) {
-    const int lane = tid & 63, wave = tid >> 6;
+    vok = rok = 0;
 #pragma unroll
     for (int i = 0; i < kVU; ++i) {
-      const int rg = wave + 4 * i;
+      const int u = tid + NT * i;
+      const int phys = u < NR * 8 ? rows[v_row(u)] : -1;
+      vok |= uint32_t(phys >= 0) << i;
+      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int phys = rows[8 * rg + e];
-        vraw[i][e] = phys >= 0
-            ? *reinterpret_cast<const u32x4*>(latent + int64_t(phys) * kStride + 16 * lane)
-            : u32x4{0, 0, 0, 0};
+      for (int m = 0; m < 8; ++m)
+        vraw[i][m] = *reinterpret_cast<const u32x4*>(row + 128 * v_grp(u) + 16 * m);
+    }
+#pragma unroll
+    for (int i = 0; i < kRU; ++i) {
+      const int u = tid + NT * i;
+      const int phys = u < NR * 4 ? rows[r_row(u)] : -1;
+      rok |= uint32_t(phys >= 0) << i;
+      const u32x4* src = reinterpret_cast<const u32x4*>(latent + int64_t(max(phys, 0)) * kStride +
+                                                        2 * DSA_D_LATENT + 32 * r_piece(u));
+      rraw[i][0] = src[0];
+      rraw[i][1] = src[1];
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* k, int r0, int tid) const {
+    const u32x4 z = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kVU; ++i) {
+      const int u = tid + NT * i;
+      const bool ok = (vok >> i) & 1u;
+      if (u < NR * 8) {
+#pragma unroll
+        for (int m = 0; m < 8; m += 2) {
+          const int r = r0 + v_row(u), sw = k_swz(r);
+          uint16_t* row = k + r * kKStride + 8 * (8 * v_grp(u) + m);
+          *reinterpret_cast<u32x4*>(row + 8 * sw) = ok ? vraw[i][m] : z;
+          *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = ok ? vraw[i][m + 1] : z;
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < kRU; ++i) {
-      const int u = tid + kThreads * i;
-      rraw[i][0] = rraw[i][1] = u32x4{0, 0, 0, 0};
-      if (u < TILE * 4) {
-        const int phys = rows[u >> 2];
-        if (phys >= 0) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(latent + int64_t(phys) * kStride +
-                                                            2 * DSA_D_LATENT + 32 * (u & 3));
-          rraw[i][0] = src[0];
-          rraw[i][1] = src[1];
-        }
+      const int u = tid + NT * i;
+      const bool ok = (rok >> i) & 1u;
+      if (u < NR * 4) {
+        const int r = r0 + r_row(u), sw = k_swz(r);
+        uint16_t* row = k + r * kKStride + 8 * (DSA_D_LATENT / 8 + 2 * r_piece(u));
+        *reinterpret_cast<u32x4*>(row + 8 * sw) = ok ? rraw[i][0] : z;
+        *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = ok ? rraw[i][1] : z;
       }
-    }
-  }
-  __device__ __forceinline__ void vbits(int i, uint32_t bits[8][4]) const {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) bits[e][m] = vraw[i][e][m];
-  }
-  __device__ __forceinline__ void rbits(int i, uint32_t bits[8]) const {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bits[m] = rraw[i][0][m];
-      bits[4 + m] = rraw[i][1][m];
     }
   }
 };
 
-template <int KV, int TILE>
-__device__ __forceinline__ void stage_store(const Stage<KV, TILE>& st, TileSmem<TILE>& sm, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < Stage<KV, TILE>::kVU; ++i) {
-    const int rg = wave + 4 * i;
-    uint32_t bits[8][4];
-    st.vbits(i, bits);
-    // row-major K: row 8rg+e, cols 8*lane .. +8
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<u32x4*>(&sm.k[(8 * rg + e) * kKStride + 8 * lane]) =
-          u32x4{bits[e][0], bits[e][1], bits[e][2], bits[e][3]};
-    // transposed V: column d = 8*lane + dd, rows 8rg .. +8
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int m = dd >> 1;
-      const bool hi = dd & 1;
-      uint32_t v[4];
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const uint32_t a = bits[2 * pr][m], b = bits[2 * pr + 1][m];
-        v[pr] = hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+// Physical rows (page*64 + slot, or -1 when masked) of index columns
+// [cc, cc + kRowChunk) of token t, written to rows[].
+__device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int req, int pos, int cc,
+                                             int cend, int32_t* rows, int tid, int nthreads) {
+  for (int i = tid; i < kRowChunk; i += nthreads) {
+    const int col = cc + i;
+    int phys = -1;
+    if (col < cend) {
+      const int p = a.idx[int64_t(t) * a.width + col];
+      if (p >= 0 && p <= pos) {
+        const int j = p >> 6;
+        if (j < a.pt_stride) {
+          int pg = a.page_table[int64_t(req) * a.pt_stride + j];
+          pg = min(max(pg, 0), a.num_pages - 1);
+          phys = pg * DSA_PAGE_TOKENS + (p & 63);
+        }
       }
-      const int d = 8 * lane + dd;
-      *reinterpret_cast<u32x4*>(&sm.vt[d * TILE + 8 * (rg ^ vt_swizzle<TILE>(d))]) =
-          u32x4{v[0], v[1], v[2], v[3]};
     }
-  }
-#pragma unroll
-  for (int i = 0; i < Stage<KV, TILE>::kRU; ++i) {
-    const int u = tid + kThreads * i;
-    if (u < TILE * 4) {
-      uint32_t bits[8];
-      st.rbits(i, bits);
-      uint16_t* dst = &sm.k[(u >> 2) * kKStride + DSA_D_LATENT + 16 * (u & 3)];
-      *reinterpret_cast<u32x4*>(dst) = u32x4{bits[0], bits[1], bits[2], bits[3]};
-      *reinterpret_cast<u32x4*>(dst + 8) = u32x4{bits[4], bits[5], bits[6], bits[7]};
-    }
+    rows[i] = phys;
   }
 }
 
+__device__ __forceinline__ int request_of(const PartialArgs& a, int t) {
+  int lo = 0, hi = a.num_reqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.q_offsets[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Online softmax of one tile for the 16 heads of a wave (lane holds rows
+// 16mb + 4g + j of head c, log2-domain scores or -inf when masked).  Updates
+// the reference max (rescaling O when it moves), the running sum, and returns
+// P as the PV A operand.
+template <int kMB, int kNB>
+__device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB], float& m_ref,
+                                             float& l_run, u32x4 (&pa)[kMB / 2], int g) {
+  float tmax = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sacc[mb][j]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if (__any(tmax > m_ref + kRescaleThreshold)) {
+    const float m_new = fmaxf(m_ref, tmax);
+    const float alpha = (m_ref == kNegInf) ? 0.f : exp2f(m_ref - m_new);
+    l_run *= alpha;
+    m_ref = m_new;
+    float aj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[nb][j] *= aj[j];
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) {
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // masked rows carry -inf; m_ref is finite whenever a row is valid
+      p[j] = sacc[mb][j] == kNegInf ? 0.f : exp2f(sacc[mb][j] - m_ref);
+      psum += p[j];
+    }
+    const int k2 = mb >> 1, half = (mb & 1) * 2;
+    pa[k2][half] = dsa::pack_bf16x2(p[0], p[1]);
+    pa[k2][half + 1] = dsa::pack_bf16x2(p[2], p[3]);
+  }
+  psum += __shfl_xor(psum, 16);
+  psum += __shfl_xor(psum, 32);
+  l_run += psum;
+}
+
+// O[16 heads x kNB*16 columns from column col0] += P V over kKS*32 rows, V read
+// transposed from the K tile, two column blocks in flight.
+template <int kKS, int kNB>
+__device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS], f32x4 (&o)[kNB],
+                                        int col0, int g, int c) {
+  // lane reads rows 32k2 + 4g + c/4 (+16), whose swizzle bit is fixed per lane
+  const int sw = (g ^ (g >> 1)) & 1;
+  const uint16_t* vbase = k + (4 * g + (c >> 2)) * kKStride + col0 +
+                          8 * ((((c & 3) >> 1)) ^ sw) + 4 * (c & 1);
+#pragma unroll
+  for (int nb = 0; nb < kNB; nb += 2) {
+    u32x4 vb[2][kKS];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int k2 = 0; k2 < kKS; ++k2) {
+        const uint16_t* vp = vbase + 32 * k2 * kKStride + 16 * (nb + e);
+        const u32x2 lo2 = lds_read_tr16(vp);
+        const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
+        vb[e][k2] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+#pragma unroll
+    for (int k2 = 0; k2 < kKS; ++k2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        o[nb + e] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[k2]), dsa::as_bf16x8(vb[e][k2]), o[nb + e]);
+  }
+}
+
+// Masks the log2-scaled scores of invalid rows with -inf.
+template <int kMB>
+__device__ __forceinline__ void scale_and_mask(f32x4 (&sacc)[kMB], const int32_t* rows, float scale,
+                                               int g) {
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool valid = rows[16 * mb + 4 * g + j] >= 0;
+      sacc[mb][j] = valid ? sacc[mb][j] * scale : kNegInf;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 8-wave kernel, tiles of 32 or 64 rows.
+constexpr int kThreads8 = 512;
+
+template <int TILE>
+struct Smem8 {
+  uint16_t k[TILE * kKStride];
+  int32_t rows[kRowChunk];
+  float xs[8][TILE / 16][4][64];   // partial S^T of each wave, lane-major
+};
+
 template <int KV, int TILE>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) TileSmem<TILE> sm;
-  constexpr int kMB = TILE / 16;   // 16-row MFMA blocks per tile
-  constexpr int kKS = TILE / 32;   // PV k-steps per tile
+__global__ __launch_bounds__(kThreads8) void partial8_kernel(PartialArgs a) {
+  static_assert(TILE == 32 || TILE == 64, "eight-wave layout covers tiles of 32 and 64 rows");
+  __shared__ __attribute__((aligned(16))) Smem8<TILE> sm;
+  constexpr int kMB = TILE / 16;
+  constexpr int kKS = TILE / 32;
+  constexpr int kQS = DSA_D_QK / 64;          // k-steps per half of the 576 dims (9)
+  constexpr int kNB = DSA_D_LATENT / 32;      // 16-column blocks per half of the 512 (16)
+
+  const int t = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = wave & 3, dh = wave >> 2;   // head group, half of the dims
+  const int g = lane >> 4, c = lane & 15;
+  const int c0 = s * a.cols_per_split;
+  const int c1 = min(a.width, c0 + a.cols_per_split);
+  const int req = request_of(a, t);
+  const int pos = a.tok_pos[t];
+
+  // Q of head 16hg + c, dims 288dh + 32ks + 8g .. +8 (MFMA B operand)
+  u32x4 qf[kQS];
+  {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+        a.q + (int64_t(t) * DSA_HEADS + 16 * hg + c) * DSA_D_QK + (DSA_D_QK / 2) * dh);
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks) qf[ks] = qsrc[ks * 4 + g];
+  }
+  // Q must be resident before the tile loop, whose body would otherwise carry
+  // the wait for these loads into every iteration (behind the row prefetch).
+  __builtin_amdgcn_s_waitcnt(0);
+  f32x4 o[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf, l_run = 0.f;
+
+  // One tile's compute: partial S^T, pair exchange, softmax, P V.
+  auto compute_tile = [&](int it) {
+    f32x4 sacc[kMB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // rows 16mb + c: swizzle bit fixed per lane; dims 288dh + 32ks + 8g
+    const uint16_t* kq = sm.k + c * kKStride + 8 * ((DSA_D_QK / 16) * dh + (g ^ k_swz(c)));
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks) {
+      u32x4 kf[kMB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+        sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[ks]), sacc[mb]);
+    }
+    // S^T = half 0 + half 1, through LDS with the partner wave
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.xs[wave][mb][j][lane] = sacc[mb][j];
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // the same sum order on both waves of the pair
+        const float other = sm.xs[wave ^ 4][mb][j][lane];
+        sacc[mb][j] = dh == 0 ? sacc[mb][j] + other : other + sacc[mb][j];
+      }
+    scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g);
+    u32x4 pa[kKS];
+    softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
+    pv_tile<kKS, kNB>(sm.k, pa, o, (DSA_D_LATENT / 2) * dh, g, c);
+  };
+
+  // Row gathers run one tile ahead of the compute (a second register stage
+  // measured slower: it pushes the kernel into spills).
+  Stage<KV, TILE, kThreads8> st;
+  for (int cc = c0; cc < c1; cc += kRowChunk) {
+    const int cend = min(c1, cc + kRowChunk);
+    __syncthreads();
+    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads8);
+    __syncthreads();
+    const int ntile = (cend - cc + TILE - 1) / TILE;
+    st.load(a.latent, sm.rows, tid);
+    st.store(sm.k, 0, tid);
+    __syncthreads();
+    for (int it = 0; it < ntile; ++it) {
+      const bool more = it + 1 < ntile;
+      if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
+      compute_tile(it);
+      __syncthreads();
+      if (more) {
+        st.store(sm.k, 0, tid);
+        __syncthreads();
+      }
+    }
+  }
+
+  const int64_t ts = int64_t(t) * a.splits + s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lj = __shfl(l_run, 4 * g + j);
+    const float inv = lj > 0.f ? 1.f / lj : 0.f;
+    float* dst = a.o_part + (ts * DSA_HEADS + 16 * hg + 4 * g + j) * DSA_D_LATENT +
+                 (DSA_D_LATENT / 2) * dh + c;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[nb][j] * inv;
+  }
+  if (g == 0 && dh == 0)
+    a.lse_part[ts * DSA_HEADS + 16 * hg + c] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
+}
+
+// ---------------------------------------------------------------------------
+// 4-wave kernel, tiles of 128 rows.
+constexpr int kThreads4 = 256;
+constexpr int kTile4 = 128;
+
+struct Smem4 {
+  uint16_t k[kTile4 * kKStride];
+  int32_t rows[kRowChunk];
+};
+
+// Rows of a 128-row tile prefetched into registers while the previous tile is
+// computed (BF16 rows are twice the bytes: half of them are loaded after).
+template <int KV>
+constexpr int prefetch_rows4() {
+  return KV == DSA_KV_BF16 ? 64 : kTile4;
+}
+
+template <int KV>
+__global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(16))) Smem4 sm;
+  constexpr int TILE = kTile4;
+  constexpr int kMB = TILE / 16;
+  constexpr int kKS = TILE / 32;
+  constexpr int kNB = DSA_D_LATENT / 16;
+  constexpr int kPR = prefetch_rows4<KV>();
 
   const int t = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int c0 = s * a.cols_per_split;
   const int c1 = min(a.width, c0 + a.cols_per_split);
-
-  int lo = 0, hi = a.num_reqs - 1;   // request of token t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.q_offsets[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  const int req = lo;
+  const int req = request_of(a, t);
   const int pos = a.tok_pos[t];
 
-  // Q of head 16*wave + c, dims 32ks + 8g .. +8 (MFMA B operand)
   u32x4 qf[DSA_D_QK / 32];
   {
     const u32x4* qsrc =
@@ -268,121 +528,58 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int ks = 0; ks < DSA_D_QK / 32; ++ks) qf[ks] = qsrc[ks * 4 + g];
   }
-  f32x4 o[DSA_D_LATENT / 16];
+  __builtin_amdgcn_s_waitcnt(0);   // Q resident before the tile loop
+  f32x4 o[kNB];
 #pragma unroll
-  for (int nb = 0; nb < DSA_D_LATENT / 16; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf, l_run = 0.f;
 
-  Stage<KV, TILE> st;
+  Stage<KV, kPR, kThreads4> st;
+  Stage<KV, (kPR < TILE ? TILE - kPR : 32), kThreads4> st2;  // tail rows (BF16 only)
   for (int cc = c0; cc < c1; cc += kRowChunk) {
     const int cend = min(c1, cc + kRowChunk);
     __syncthreads();
-    for (int i = tid; i < kRowChunk; i += kThreads) {
-      const int col = cc + i;
-      int phys = -1;
-      if (col < cend) {
-        const int p = a.idx[int64_t(t) * a.width + col];
-        if (p >= 0 && p <= pos) {
-          const int j = p >> 6;
-          if (j < a.pt_stride) {
-            int pg = a.page_table[int64_t(req) * a.pt_stride + j];
-            pg = min(max(pg, 0), a.num_pages - 1);
-            phys = pg * DSA_PAGE_TOKENS + (p & 63);
-          }
-        }
-      }
-      sm.rows[i] = phys;
-    }
+    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads4);
     __syncthreads();
     const int ntile = (cend - cc + TILE - 1) / TILE;
     st.load(a.latent, sm.rows, tid);
-    stage_store<KV, TILE>(st, sm, tid);
+    st.store(sm.k, 0, tid);
+    if constexpr (kPR < TILE) {
+      st2.load(a.latent, sm.rows + kPR, tid);
+      st2.store(sm.k, kPR, tid);
+    }
     __syncthreads();
     for (int it = 0; it < ntile; ++it) {
       const bool more = it + 1 < ntile;
       if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
 
-      // ---- S^T = K Q^T for this wave's 16 heads
       f32x4 sacc[kMB];
+      const uint16_t* kq = sm.k + c * kKStride + 8 * (g ^ k_swz(c));
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = &sm.k[(16 * mb + c) * kKStride + 8 * g];
 #pragma unroll
         for (int ks = 0; ks < DSA_D_QK / 32; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 32 * ks);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
           sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[ks]), sacc[mb]);
         }
       }
-
-      // ---- online softmax (log2 domain); lane holds rows 16mb+4g+j of head c
-      const int32_t* rows = sm.rows + it * TILE;
-      float z[kMB][4];
-      float tmax = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool valid = rows[16 * mb + 4 * g + j] >= 0;
-          z[mb][j] = valid ? sacc[mb][j] * a.scale_log2 : kNegInf;
-          tmax = fmaxf(tmax, z[mb][j]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const bool none = (m_new == kNegInf);
-      const float alpha = none ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
-      float p[kMB][4];
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[mb][j] = none ? 0.f : exp2f(z[mb][j] - m_new);
-          psum += p[mb][j];
-        }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      float aj[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j);
-#pragma unroll
-      for (int nb = 0; nb < DSA_D_LATENT / 16; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[nb][j] *= aj[j];
-
-      // ---- O += P V : P straight from the S^T accumulators
+      scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g);
       u32x4 pa[kKS];
-#pragma unroll
-      for (int k2 = 0; k2 < kKS; ++k2)
-        pa[k2] = u32x4{dsa::pack_bf16x2(p[2 * k2][0], p[2 * k2][1]),
-                       dsa::pack_bf16x2(p[2 * k2][2], p[2 * k2][3]),
-                       dsa::pack_bf16x2(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
-                       dsa::pack_bf16x2(p[2 * k2 + 1][2], p[2 * k2 + 1][3])};
-#pragma unroll
-      for (int nb = 0; nb < DSA_D_LATENT / 16; ++nb) {
-        const int d = 16 * nb + c;
-        const int sw = vt_swizzle<TILE>(d);
-        const uint16_t* vrow = &sm.vt[d * TILE + 4 * (g & 1)];
-#pragma unroll
-        for (int k2 = 0; k2 < kKS; ++k2) {
-          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + 8 * ((4 * k2 + (g >> 1)) ^ sw));
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + 8 * ((4 * k2 + 2 + (g >> 1)) ^ sw));
-          const u32x4 vb = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-          o[nb] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[k2]), dsa::as_bf16x8(vb), o[nb]);
-        }
-      }
+      softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
+      pv_tile<kKS, kNB>(sm.k, pa, o, 0, g, c);
       __syncthreads();
       if (more) {
-        stage_store<KV, TILE>(st, sm, tid);
+        st.store(sm.k, 0, tid);
+        if constexpr (kPR < TILE) {
+          st2.load(a.latent, sm.rows + (it + 1) * TILE + kPR, tid);
+          st2.store(sm.k, kPR, tid);
+        }
         __syncthreads();
       }
     }
   }
 
-  // ---- normalize and write this split's partial
   const int64_t ts = int64_t(t) * a.splits + s;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -390,16 +587,18 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     const float inv = lj > 0.f ? 1.f / lj : 0.f;
     float* dst = a.o_part + (ts * DSA_HEADS + 16 * wave + 4 * g + j) * DSA_D_LATENT + c;
 #pragma unroll
-    for (int nb = 0; nb < DSA_D_LATENT / 16; ++nb) dst[16 * nb] = o[nb][j] * inv;
+    for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[nb][j] * inv;
   }
   if (g == 0)
-    a.lse_part[ts * DSA_HEADS + 16 * wave + c] =
-        l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : kNegInf;
+    a.lse_part[ts * DSA_HEADS + 16 * wave + c] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
 }
 
 template <int KV, int TILE>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
-  hipLaunchKernelGGL((partial_kernel<KV, TILE>), dim3(T, S), dim3(kThreads), 0, st, a);
+  if constexpr (TILE == kTile4)
+    hipLaunchKernelGGL((partial4_kernel<KV>), dim3(T, S), dim3(kThreads4), 0, st, a);
+  else
+    hipLaunchKernelGGL((partial8_kernel<KV, TILE>), dim3(T, S), dim3(kThreads8), 0, st, a);
   return hipGetLastError();
 }
 
@@ -463,8 +662,6 @@ extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t
   if (!dsa::aligned(q, 16) || !dsa::aligned(idx, 4) || !dsa::aligned(o_part, 16) ||
       !dsa::aligned(lse_part, 4))
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: q and o_part must be 16-byte aligned");
-  if (kv_tile == 128)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_partial: kv_tile 128 is not built yet");
   dsa_partial_plan plan;
   if (dsa_plan_partial(num_tokens, width, kv_tile, num_splits, 0, &plan) != DSA_OK)
     return DSA_ERR_INVALID_ARG;
@@ -490,9 +687,12 @@ extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t
   if (kv_tile == 32)
     e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 32>(a, num_tokens, num_splits, st)
             : launch_partial<DSA_KV_BF16, 32>(a, num_tokens, num_splits, st);
-  else
+  else if (kv_tile == 64)
     e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 64>(a, num_tokens, num_splits, st)
             : launch_partial<DSA_KV_BF16, 64>(a, num_tokens, num_splits, st);
+  else
+    e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 128>(a, num_tokens, num_splits, st)
+            : launch_partial<DSA_KV_BF16, 128>(a, num_tokens, num_splits, st);
   if (e != hipSuccess)
     return dsa::fail(DSA_ERR_HIP, std::string("dsa_sparse_mla_partial: launch failed: ") +
                                       hipGetErrorString(e));
