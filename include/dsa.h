@@ -168,7 +168,8 @@ dsa_status dsa_index_scores(const dsa_pool* pool, const int32_t* page_table, int
  * than k positions are visible.  Scores are compared as fp32 (NaN unsupported).
  * Rows longer than 65,536 positions use `workspace` (device, 256-byte
  * aligned) of at least dsa_topk_workspace_bytes() bytes; 0 bytes otherwise.
- * Limits: 1 <= k <= 16384; max_ctx <= 65536 * (65536 / k). */
+ * Limits: 1 <= k <= 16384; max_ctx <= 65536 * (65536 / k) (2,097,152 at
+ * k = 2048). */
 size_t dsa_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t k);
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos, int32_t num_tokens,
                     int32_t max_ctx, int32_t k, int32_t* idx, void* workspace,

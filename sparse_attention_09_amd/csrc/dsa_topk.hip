@@ -7,15 +7,21 @@
 // documented with the oracle).
 //
 // One 1024-thread workgroup selects from up to 65,536 elements held in
-// registers (64 per thread, loaded once with coalesced loads):
-//   1. map each fp32 to an order-preserving uint32 key (invalid -> 0);
-//   2. radix-select the k-th largest key over the key range actually present
-//      (up to three 11-bit passes with LDS histograms; only elements still
-//      matching the selected prefix take part in later passes);
-//   3. mark the keys above the threshold and the keys equal to it in two LDS
-//      bitmaps; a block scan over per-thread popcounts keeps the lowest-position
-//      equal keys that fit, and a second scan writes the selected positions in
-//      ascending order.
+// registers (64 per thread; element e = 1024*i + tid, loaded with coalesced
+// dword loads).  Scores map to order-preserving uint32 keys (invalid -> 0).
+//   1. while loading, a 4096-bin LDS histogram of the keys' top 12 bits
+//      (sign, exponent, 3 mantissa bits) is built;
+//   2. a block suffix scan finds the bin holding the k-th largest key; one
+//      pass over the registers marks keys above that bin in an LDS bitmap and
+//      appends the bin's keys to an LDS candidate list (rare predicated LDS
+//      atomics);
+//   3. two 10-bit histogram passes over the candidates only give the exact
+//      threshold key and how many keys equal to it are kept (a bin too wide
+//      for the list falls back to the same passes over the registers);
+//   4. candidates above the threshold and those equal to it go to LDS
+//      bitmaps; a block scan over per-thread popcounts keeps the
+//      lowest-position equal keys that fit, and a second scan writes the
+//      selected positions in ascending order.
 // Longer rows are cut into 65,536-position segments whose local top-k
 // candidates (kept in ascending position order) are merged by a second pass
 // of the same kernel: the global top-k under (score desc, position asc) is
@@ -31,8 +37,11 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kEPT = 64;                       // elements per thread
 constexpr int kSeg = kThreads * kEPT;          // 65536
-constexpr int kBins = 2048;
 constexpr int kWords = kSeg / 32;              // bitmap words
+constexpr int kCoarseBits = 12;                // top key bits of the first histogram
+constexpr int kBins = 1 << kCoarseBits;        // 4096
+constexpr int kFineBits = 10;                  // 32 - 12 = 20 remaining bits = 2 x 10
+constexpr int kCap = 4096;                     // threshold-bin candidates kept in LDS
 
 static_assert(kSeg == dsa::kTopkSeg, "segment size must match the host side");
 
@@ -42,9 +51,11 @@ struct Smem {
   uint32_t hist[kBins];
   uint32_t gt_bits[kWords];
   uint32_t eq_bits[kWords];
+  uint32_t cand_key[kCap];                     // keys of the threshold bin
+  uint32_t cand_idx[kCap];                     // their element indices
   uint32_t wave_tmp[kWaves];
   uint32_t red[4];
-  uint32_t sel_digit, sel_above;
+  uint32_t sel_digit, sel_above, cand_n;
 };
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
@@ -76,19 +87,36 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, Smem& sm, uint32
   return res;
 }
 
+// Finds the bin (of nbins <= kBins, from the top) holding the k_rem-th largest
+// key; writes sel_digit and sel_above (count in higher bins).  Thread i looks
+// at bins [nbins - (i+1)*per, nbins - i*per).  Contains barriers; the result
+// is readable after it returns.
+__device__ __forceinline__ void select_bin(Smem& sm, uint32_t k_rem, int nbins, int tid) {
+  const int per = nbins / kThreads > 0 ? nbins / kThreads : 1;
+  const int top = nbins - per * tid;           // exclusive upper bin of this thread
+  uint32_t local = 0;
+  if (top > 0)
+    for (int b = top - 1; b >= top - per; --b) local += sm.hist[b];
+  uint32_t tot;
+  const uint32_t above = block_excl_scan(local, sm, &tot);
+  if (top > 0 && above < k_rem && k_rem <= above + local) {
+    uint32_t acc = above;
+    for (int b = top - 1; b >= top - per; --b) {
+      const uint32_t h = sm.hist[b];
+      if (acc + h >= k_rem) {
+        sm.sel_digit = uint32_t(b);
+        sm.sel_above = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off));
   return v;
 }
 
@@ -107,8 +135,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int32_t* vpos = nullptr;  // merge mode: candidate positions
   if (MODE == kSegment) {
     t = blockIdx.y;
-    const int seg = blockIdx.x;
-    base = seg * kSeg;
+    base = blockIdx.x * kSeg;
     const int vis = min(tok_pos[t], max_ctx - 1) + 1;
     n = max(0, min(vis - base, kSeg));
     vals = scores + int64_t(t) * ld + base;
@@ -123,116 +150,140 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     vals = scores + int64_t(t) * ld;
   }
 
-  // ---- load keys: element e = 1024*i + tid (each wave load reads 256
-  // contiguous bytes; a wave's ballot over one i covers 64 consecutive elements)
+  for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
+  if (tid == 0) sm.cand_n = 0;
+  __syncthreads();
+
+  // ---- load keys and build the coarse histogram.  Loads are unconditional
+  // (clamped into the row, which always holds an element) so all are in flight.
   uint32_t key[kEPT];
-  uint32_t my_valid = 0, my_min = 0xffffffffu, my_max = 0;
-  // Loads are unconditional (clamped into the row, which always holds at least
-  // one element) so that all of them are in flight at once; the element count
-  // of this thread decides validity.
   const int cnt = n > tid ? (n - tid + kThreads - 1) / kThreads : 0;
   const int last = max(n - 1, 0);
-  float v[kEPT];
-  int pv[kEPT];
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
     const int e = min(kThreads * i + tid, last);
-    v[i] = vals[e];
-    if (MODE == kMerge) pv[i] = vpos[e];
+    key[i] = __float_as_uint(vals[e]);
   }
+  uint32_t my_valid = 0;
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
-    uint32_t valid = 0u - uint32_t(i < cnt);                 // all-ones when valid
-    if (MODE == kMerge) valid &= 0u - uint32_t(pv[i] >= 0);
-    const uint32_t kk = dsa::float_key(v[i]) & valid;
-    key[i] = kk;
-    my_valid += valid & 1u;
-    my_min = min(my_min, kk | ~valid);
-    my_max = max(my_max, kk);
+    bool ok = i < cnt;
+    if (MODE == kMerge) ok = ok && vpos[min(kThreads * i + tid, last)] >= 0;
+    key[i] = ok ? dsa::float_key(__uint_as_float(key[i])) : 0u;
+    my_valid += ok ? 1u : 0u;
+    if (ok) atomicAdd(&sm.hist[key[i] >> (32 - kCoarseBits)], 1u);
   }
-
-  // ---- count, min and max of the valid keys
   {
-    uint32_t a = wave_sum(my_valid), b = wave_min(my_min), c = wave_max(my_max);
-    if (lane == 0) {
-      sm.hist[wave] = a;
-      sm.hist[kWaves + wave] = b;
-      sm.hist[2 * kWaves + wave] = c;
-    }
+    const uint32_t a = wave_sum(my_valid);
+    if (lane == 0) sm.wave_tmp[wave] = a;
     __syncthreads();
     if (tid == 0) {
-      uint32_t s = 0, mn = 0xffffffffu, mx = 0;
-      for (int i = 0; i < kWaves; ++i) {
-        s += sm.hist[i];
-        mn = min(mn, sm.hist[kWaves + i]);
-        mx = max(mx, sm.hist[2 * kWaves + i]);
-      }
-      sm.red[0] = s;
-      sm.red[1] = mn;
-      sm.red[2] = mx;
+      uint32_t tot = 0;
+      for (int i = 0; i < kWaves; ++i) tot += sm.wave_tmp[i];
+      sm.red[0] = tot;
     }
     __syncthreads();
   }
   const uint32_t n_valid = sm.red[0];
-  const uint32_t kmin = sm.red[1], kmax = sm.red[2];
 
-  // ---- threshold key tau and the number r of tau-equal keys to keep
-  uint32_t tau = 0, r = 0;  // tau = 0, r = 0 keeps every valid key
+  // ---- threshold key tau (the k-th largest key), the number r of tau-equal
+  // keys to keep, and the bitmaps of kept keys above tau / equal to tau
+  uint32_t tau = 0, r = 0;   // tau = 0, r = 0 keeps every valid key
+  bool bitmaps_done = false;
   if (n_valid > uint32_t(k)) {
-    const uint32_t range = kmax - kmin;
-    int hi = range ? 32 - __clz(range) : 0;  // bits of (key - kmin) still undecided
-    uint32_t prefix = 0;                      // decided high bits of (key - kmin)
     uint32_t k_rem = uint32_t(k);
-    while (hi > 0) {
-      const int nbits = hi < 11 ? hi : 11;
-      const int shift = hi - nbits;
-      const uint32_t dmask = (1u << nbits) - 1u;
-      for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
+    select_bin(sm, k_rem, kBins, tid);
+    const uint32_t dsel = sm.sel_digit;
+    const uint32_t nsel = sm.hist[dsel];
+    k_rem -= sm.sel_above;
+    uint32_t prefix = dsel;            // decided high bits of the threshold key
+    int hi = 32 - kCoarseBits;         // bits still undecided
+    __syncthreads();
+    if (nsel <= uint32_t(kCap)) {
+      // keys above the bin are kept; the bin's keys become LDS candidates
+      for (int i = tid; i < kWords; i += kThreads) {
+        sm.gt_bits[i] = 0;
+        sm.eq_bits[i] = 0;
+      }
       __syncthreads();
+      // element 1024e + tid: bitmap word 32e + tid/32, bit tid%32
+      uint32_t* gt_word = &sm.gt_bits[tid >> 5];
+      const uint32_t bit = 1u << (tid & 31);
 #pragma unroll
       for (int e = 0; e < kEPT; ++e) {
-        const uint32_t kk = key[e];
-        const uint32_t rel = kk - kmin;
-        const bool cand = kk != 0 && (hi >= 32 ? true : ((rel >> hi) == prefix));
-        const uint32_t d = (rel >> shift) & dmask;
-        if (cand) atomicAdd(&sm.hist[d], 1u);
+        const uint32_t d = key[e] >> hi;
+        if (key[e] != 0 && d >= dsel) {
+          if (d > dsel) {
+            atomicOr(gt_word + 32 * e, bit);
+          } else {
+            const uint32_t slot = atomicAdd(&sm.cand_n, 1u);
+            sm.cand_key[slot] = key[e];
+            sm.cand_idx[slot] = uint32_t(kThreads * e + tid);
+          }
+        }
       }
       __syncthreads();
-      // suffix search from the top bin: thread i looks at bins (2047-2i, 2046-2i)
-      const int bhi = kBins - 1 - 2 * tid, blo = bhi - 1;
-      const uint32_t hh = sm.hist[bhi], hl = sm.hist[blo];
-      uint32_t tot;
-      const uint32_t above = block_excl_scan(hh + hl, sm, &tot);
-      if (above < k_rem && k_rem <= above + hh) {
-        sm.sel_digit = uint32_t(bhi);
-        sm.sel_above = above;
-      } else if (above + hh < k_rem && k_rem <= above + hh + hl) {
-        sm.sel_digit = uint32_t(blo);
-        sm.sel_above = above + hh;
+      // refine among the candidates only
+      while (hi > 0) {
+        const int sh = hi - kFineBits;
+        for (int i = tid; i < (1 << kFineBits); i += kThreads) sm.hist[i] = 0;
+        __syncthreads();
+        for (uint32_t j = tid; j < nsel; j += kThreads) {
+          const uint32_t c = sm.cand_key[j];
+          if ((c >> hi) == prefix) atomicAdd(&sm.hist[(c >> sh) & ((1u << kFineBits) - 1u)], 1u);
+        }
+        __syncthreads();
+        select_bin(sm, k_rem, 1 << kFineBits, tid);
+        prefix = (prefix << kFineBits) | sm.sel_digit;
+        k_rem -= sm.sel_above;
+        hi = sh;
+        __syncthreads();
       }
-      __syncthreads();
-      prefix = (prefix << nbits) | sm.sel_digit;
-      k_rem -= sm.sel_above;
-      hi = shift;
-      __syncthreads();
+      // mark the candidates kept: above the exact threshold, or equal to it
+      for (uint32_t j = tid; j < nsel; j += kThreads) {
+        const uint32_t c = sm.cand_key[j], ei = sm.cand_idx[j];
+        if (c > prefix) atomicOr(&sm.gt_bits[ei >> 5], 1u << (ei & 31));
+        else if (c == prefix) atomicOr(&sm.eq_bits[ei >> 5], 1u << (ei & 31));
+      }
+      bitmaps_done = true;
+    } else {
+      // wide threshold bin (heavy ties): refine over the registers
+      while (hi > 0) {
+        const int sh = hi - kFineBits;
+        for (int i = tid; i < (1 << kFineBits); i += kThreads) sm.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kEPT; ++e) {
+          const uint32_t c = key[e];
+          if (c != 0 && (c >> hi) == prefix) atomicAdd(&sm.hist[(c >> sh) & ((1u << kFineBits) - 1u)], 1u);
+        }
+        __syncthreads();
+        select_bin(sm, k_rem, 1 << kFineBits, tid);
+        prefix = (prefix << kFineBits) | sm.sel_digit;
+        k_rem -= sm.sel_above;
+        hi = sh;
+        __syncthreads();
+      }
     }
-    tau = kmin + prefix;
+    tau = prefix;
     r = k_rem;
   }
 
-  // ---- bitmaps of keys above tau and keys equal to tau (one ballot per
-  // 64 consecutive elements, written by lane 0; no atomics)
+  if (!bitmaps_done) {
+    // bitmaps straight from the registers: one ballot per 64 consecutive
+    // elements, written by lane 0 (no atomics)
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) {
-    const uint32_t kk = key[i];
-    const uint64_t mg = __ballot(kk > tau);
-    const uint64_t me = __ballot(r > 0 && kk == tau);
-    if (lane == 0) {
-      const int wd = (kThreads * i + 64 * wave) >> 5;
-      sm.gt_bits[wd] = uint32_t(mg);
-      sm.gt_bits[wd + 1] = uint32_t(mg >> 32);
-      sm.eq_bits[wd] = uint32_t(me);
-      sm.eq_bits[wd + 1] = uint32_t(me >> 32);
+    for (int i = 0; i < kEPT; ++i) {
+      const uint32_t kk = key[i];
+      const uint64_t mg = __ballot(kk > tau);
+      const uint64_t me = __ballot(r > 0 && kk == tau);
+      if (lane == 0) {
+        const int wd = (kThreads * i + 64 * wave) >> 5;
+        sm.gt_bits[wd] = uint32_t(mg);
+        sm.gt_bits[wd + 1] = uint32_t(mg >> 32);
+        sm.eq_bits[wd] = uint32_t(me);
+        sm.eq_bits[wd + 1] = uint32_t(me >> 32);
+      }
     }
   }
   __syncthreads();

@@ -200,3 +200,23 @@ def test_topk_long_rows_two_stage():
     for t in range(T):
         ref = O.topk_positions(sc[t, :int(tok_pos[t]) + 1].numpy(), k)
         assert np.array_equal(idx[t], ref), t
+
+
+def test_topk_full_rows_candidate_and_fallback_paths():
+    # 65,536-position rows: (a) integer scores like the indexer's (threshold bin
+    # small enough for the LDS candidate list), (b) three distinct values (the
+    # threshold bin overflows the list: register fallback), (c) negative and
+    # positive values with many exact ties, (d) a row shorter than k
+    L, k = 65536, 2048
+    g = torch.Generator().manual_seed(13)
+    rows = [torch.randint(0, 15000, (L,), generator=g).float(),
+            torch.randint(0, 3, (L,), generator=g).float() * 7.0,
+            (torch.randint(-50, 50, (L,), generator=g).float() * 0.25),
+            torch.randn(L, generator=g)]
+    sc = torch.stack(rows)
+    tok_pos = torch.tensor([L - 1, L - 1, 40000, 1000], dtype=torch.int32)
+    say("[case] topk full rows")
+    idx = dsa.topk(sc.to(DEV), tok_pos.to(DEV), k, L).cpu().numpy()
+    for t in range(sc.shape[0]):
+        ref = O.topk_positions(sc[t, :int(tok_pos[t]) + 1].numpy(), k)
+        assert np.array_equal(idx[t], ref), t

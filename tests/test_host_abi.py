@@ -185,6 +185,7 @@ def test_topk_workspace_bytes():
     assert L.dsa_topk_workspace_bytes(1024, 65536, 2048) == 0
     # 1M positions -> 16 segments of 65,536, candidates of (fp32, int32)
     assert L.dsa_topk_workspace_bytes(8, 1 << 20, 2048) == 8 * 16 * 2048 * 8
+    # k is padded to a multiple of 4 per segment
     assert L.dsa_topk_workspace_bytes(2, 70000, 5) == 2 * 2 * 8 * 8
 
 
