@@ -7,6 +7,8 @@ each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
 64 heads.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --summarize-stats KERNEL_STATS_CSV COMMAND...      (rocprofv3 summary text)
+  python bench.py --summarize-pmc FETCH_CSV WRITE_CSV WORKLOAD CMD... (traffic JSON)
 """
 
 from __future__ import annotations
@@ -54,7 +56,7 @@ def flops(spec):
     return {"index_scores": vis * 16 * 128 * 2, "partial": T * 64 * k * (576 + 512) * 2}
 
 
-def cpu_baseline(wl, budget_s=12.0, max_tokens=64):
+def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
     """The oracle, as written, on a bounded sample of the same workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -95,7 +97,106 @@ def cpu_baseline(wl, budget_s=12.0, max_tokens=64):
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 
+KERNEL_PATTERNS = {"index_scores": "index_scores", "topk": "topk_kernel", "partial": "partial",
+                   "combine": "combine_kernel"}
+KERNEL_SOURCES = {"index_scores": "dsa_index.hip", "topk": "dsa_topk.hip",
+                  "partial": "dsa_partial.hip", "combine": "dsa_partial.hip"}
+CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
+
+
+def source_sha(kernel: str) -> str:
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "dsa_device.h"):
+        with open(os.path.join(root, "sparse_attention_09_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_of(name: str):
+    for k, pat in KERNEL_PATTERNS.items():
+        if pat in name:
+            return k
+    return None
+
+
+def summarize_stats(csv_path: str, command: str) -> str:
+    """Text summary of a rocprofv3 --stats kernel table."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "#",
+             f"{'kernel':14s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}  name"]
+    for r in rows:
+        k = _kernel_of(r["Name"])
+        if k is None:
+            continue
+        lines.append(f"{k:14s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}  {r['Name'][:90]}")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands: list) -> dict:
+    """Per-launch HBM traffic of each path kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), scaled by what the same counters read for a copy of
+    known size (1 GiB read + 1 GiB written by an elementwise negation)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals, calib = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "neg" in r["Kernel_Name"].lower():
+                calib.append(v)
+                continue
+            k = _kernel_of(r["Kernel_Name"])
+            if k is not None:
+                vals.setdefault(k, []).append(v)
+        return {k: statistics.median(v) for k, v in vals.items()}, statistics.median(calib)
+
+    fetch, cf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, cw = per_kernel(write_csv, "WRITE_SIZE")
+    f_fetch = CALIB_BYTES / (cf * 1024.0)
+    f_write = CALIB_BYTES / (cw * 1024.0)
+    out = {"workload": workload, "commands": commands,
+           "calibration": {"bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+                           "fetch_kib": cf, "write_kib": cw, "factor_fetch": f_fetch,
+                           "factor_write": f_write},
+           "kernels": {}}
+    for k in sorted(set(fetch) | set(write)):
+        fb = fetch.get(k, 0.0) * 1024.0 * f_fetch
+        wb = write.get(k, 0.0) * 1024.0 * f_write
+        out["kernels"][k] = {"fetch_kib": fetch.get(k), "write_kib": write.get(k),
+                             "read_bytes": int(fb), "write_bytes": int(wb),
+                             "traffic_bytes": int(fb + wb), "source_sha": source_sha(k)}
+    return out
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    import json as _json
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = _json.load(open(path)).get("kernels", {}).get(kernel)
+    if not d or d.get("source_sha") != source_sha(kernel):
+        return None
+    return d["traffic_bytes"]
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
+        print(summarize_stats(sys.argv[2], " ".join(sys.argv[3:])), end="")
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        fetch_csv, write_csv, workload = sys.argv[2:5]
+        print(json.dumps(summarize_pmc(fetch_csv, write_csv, workload, sys.argv[5:]), indent=1))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -105,6 +206,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
+                         "(reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -180,8 +284,11 @@ def main():
     T = spec.num_tokens
     value = T / (ms_step * 1e-3)
     roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(kernels[dom]["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(kernels[dom]["gbps"] / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(spec.name, dom),
             "alg_bytes_per_launch": int(byts[dom]), "avg_us": kernels[dom]["avg_us"]}
+    for n in names:
+        kernels[n]["traffic_bytes"] = measured_traffic(spec.name, n)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
@@ -197,6 +304,12 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    if args.calibrate_copy:
+        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl)
