@@ -22,7 +22,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kQB = 8;             // query tokens per workgroup
-constexpr int kChunkPages = 8;     // pages per workgroup
+#ifndef DSA_INDEX_CHUNK_PAGES
+#define DSA_INDEX_CHUNK_PAGES 8
+#endif
+constexpr int kChunkPages = DSA_INDEX_CHUNK_PAGES;   // pages per workgroup
 constexpr int kKeyStride = 136;    // LDS stride of one key row in bf16 (128 + 8 pad)
 constexpr int kPageKeysBf16 = DSA_PAGE_TOKENS * DSA_IDX_DIM;
 
@@ -103,13 +106,15 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     id = min(max(id, 0), num_pages - 1);
     return reinterpret_cast<const u32x4*>(keys + int64_t(id) * kPageKeysBf16);
   };
-  u32x4 pre[4];
-  auto load_page = [&](int pg) {
+  // two register stages: page pg+1 is in flight in one while page pg+2 is
+  // requested into the other (the stages alternate, so the loop is unrolled by 2)
+  u32x4 pa[4], pb[4];
+  auto load_page = [&](u32x4 (&pre)[4], int pg) {
     const u32x4* src = page_src(pg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pre[i] = src[tid + kThreads * i];
   };
-  auto store_page = [&](int buf) {
+  auto store_page = [&](const u32x4 (&pre)[4], int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int piece = tid + kThreads * i;
@@ -118,13 +123,18 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     }
   };
 
-  load_page(page_begin);
-  store_page(0);
+  load_page(pa, page_begin);
+  if (page_begin + 1 < page_end) load_page(pb, page_begin + 1);
+  store_page(pa, 0);
   __syncthreads();
   int cur = 0;
   for (int pg = page_begin; pg < page_end; ++pg) {
+    // pb holds page pg+1 (if any) when an even step starts, pa when an odd one does
+    const bool odd = ((pg - page_begin) & 1) != 0;
     const bool more = pg + 1 < page_end;
-    if (more) load_page(pg + 1);
+    if (pg + 2 < page_end) {
+      if (odd) load_page(pb, pg + 2); else load_page(pa, pg + 2);
+    }
     if (wave_active) {
       const int pos0 = pg * DSA_PAGE_TOKENS;
       for (int nb = sub; nb < 4; nb += nsub) {
@@ -151,7 +161,9 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
         if (g == 1 && hasB && p <= posB) scores[int64_t(tB) * ld + p] = sB;
       }
     }
-    if (more) store_page(cur ^ 1);
+    if (more) {
+      if (odd) store_page(pa, cur ^ 1); else store_page(pb, cur ^ 1);
+    }
     __syncthreads();
     cur ^= 1;
   }

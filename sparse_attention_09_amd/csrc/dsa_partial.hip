@@ -296,7 +296,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB]
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   if (__any(tmax > m_ref + kRescaleThreshold)) {
     const float m_new = fmaxf(m_ref, tmax);
-    const float alpha = (m_ref == kNegInf) ? 0.f : exp2f(m_ref - m_new);
+    const float alpha = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
     l_run *= alpha;
     m_ref = m_new;
     float aj[4];
@@ -314,7 +314,8 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // masked rows carry -inf; m_ref is finite whenever a row is valid
-      p[j] = sacc[mb][j] == kNegInf ? 0.f : exp2f(sacc[mb][j] - m_ref);
+      // v_exp_f32: arguments are <= 8, results flush to 0 far below the max
+      p[j] = sacc[mb][j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sacc[mb][j] - m_ref);
       psum += p[j];
     }
     const int k2 = mb >> 1, half = (mb & 1) * 2;
@@ -355,17 +356,34 @@ __device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS
   }
 }
 
-// Masks the log2-scaled scores of invalid rows with -inf.
+// Scales S^T into the log2 domain and masks invalid rows (-1 in rows[]) with
+// -inf.  Rows 16mb + 4g + j of the tile are held by this lane; validity comes
+// from one ballot per 64 rows, and fully valid tiles skip the masking.
 template <int kMB>
 __device__ __forceinline__ void scale_and_mask(f32x4 (&sacc)[kMB], const int32_t* rows, float scale,
-                                               int g) {
+                                               int g, int lane) {
+  constexpr int TILE = kMB * 16;
+  uint64_t valid[(TILE + 63) / 64];
+#pragma unroll
+  for (int h = 0; h < (TILE + 63) / 64; ++h)
+    valid[h] = __ballot((h * 64 + lane < TILE) && rows[h * 64 + lane] >= 0);
+  bool all = true;
+#pragma unroll
+  for (int h = 0; h < (TILE + 63) / 64; ++h)
+    all = all && (valid[h] == (TILE - 64 * h >= 64 ? ~0ull : ((1ull << (TILE - 64 * h)) - 1ull)));
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool valid = rows[16 * mb + 4 * g + j] >= 0;
-      sacc[mb][j] = valid ? sacc[mb][j] * scale : kNegInf;
-    }
+    for (int j = 0; j < 4; ++j) sacc[mb][j] *= scale;
+  if (!all) {
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * mb + 4 * g + j;
+        if (!((valid[r >> 6] >> (r & 63)) & 1ull)) sacc[mb][j] = kNegInf;
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +394,7 @@ template <int TILE>
 struct Smem8 {
   uint16_t k[TILE * kKStride];
   int32_t rows[kRowChunk];
-  float xs[8][TILE / 16][4][64];   // partial S^T of each wave, lane-major
+  f32x4 xs[8][TILE / 16][64];      // partial S^T of each wave, lane-major
 };
 
 template <int KV, int TILE>
@@ -431,19 +449,16 @@ __global__ __launch_bounds__(kThreads8) void partial8_kernel(PartialArgs a) {
     }
     // S^T = half 0 + half 1, through LDS with the partner wave
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sm.xs[wave][mb][j][lane] = sacc[mb][j];
+    for (int mb = 0; mb < kMB; ++mb) sm.xs[wave][mb][lane] = sacc[mb];
     __syncthreads();
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kMB; ++mb) {
+      const f32x4 other = sm.xs[wave ^ 4][mb][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // the same sum order on both waves of the pair
-        const float other = sm.xs[wave ^ 4][mb][j][lane];
-        sacc[mb][j] = dh == 0 ? sacc[mb][j] + other : other + sacc[mb][j];
-      }
-    scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g);
+      for (int j = 0; j < 4; ++j)   // the same sum order on both waves of the pair
+        sacc[mb][j] = dh == 0 ? sacc[mb][j] + other[j] : other[j] + sacc[mb][j];
+    }
+    scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g, lane);
     u32x4 pa[kKS];
     softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
     pv_tile<kKS, kNB>(sm.k, pa, o, (DSA_D_LATENT / 2) * dh, g, c);
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
           sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[ks]), sacc[mb]);
         }
       }
-      scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g);
+      scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g, lane);
       u32x4 pa[kKS];
       softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
       pv_tile<kKS, kNB>(sm.k, pa, o, 0, g, c);
