@@ -200,8 +200,9 @@ dsa_status dsa_plan_partial(int32_t num_tokens, int32_t width, int32_t kv_tile,
  * padding) are skipped, repeats count each time.  The index tensor is
  * consumed as is: width need not be a multiple of the tile (the loop's last
  * tile is padded virtually).  A split with no valid column yields o = 0,
- * lse = -inf.  kv_tile and num_splits must be the resolved values of a plan
- * (kv_tile in {32, 64, 128}; num_splits >= 1).
+ * lse = -inf.  sm_scale must be finite and > 0.  kv_tile and num_splits
+ * must be the resolved values of a plan (kv_tile in {32, 64, 128};
+ * num_splits >= 1).
  * q: bf16 [num_tokens,64,576]; idx: int32 [num_tokens,width];
  * o_part: fp32 [num_tokens,num_splits,64,512]; lse_part: fp32
  * [num_tokens,num_splits,64].  All 16-byte aligned. */

@@ -51,6 +51,24 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t codes, float out[4]) {
   out[3] = hi[1];
 }
 
+// Max / sum over lanes i, i^16, i^32, i^48 (the four 16-lane rows of a
+// wave), every lane receiving the result: v_permlane32_swap then
+// v_permlane16_swap each pair a lane with its partner in one VALU op (no LDS
+// round trip, unlike ds_bpermute).  Both combines commute, so all four lanes
+// hold the same bits.
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
   const uint32_t u = __float_as_uint(f);

@@ -152,10 +152,8 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
           sA = fmaf(wa[j], fmaxf(accA[j], 0.f), sA);
           sB = fmaf(wb[j], fmaxf(accB[j], 0.f), sB);
         }
-        sA += __shfl_xor(sA, 16);
-        sB += __shfl_xor(sB, 16);
-        sA += __shfl_xor(sA, 32);
-        sB += __shfl_xor(sB, 32);
+        sA = dsa::rows4_sum(sA);   // integer-valued: exact in any order
+        sB = dsa::rows4_sum(sB);
         const int p = pos0 + nb * 16 + c;
         if (g == 0 && p <= posA) scores[int64_t(tA) * ld + p] = sA;
         if (g == 1 && hasB && p <= posB) scores[int64_t(tB) * ld + p] = sB;

@@ -9,29 +9,25 @@
 // 64 heads - which makes QK^T and PV dense enough for the matrix cores.
 //
 // One workgroup = one (token, split).  Per KV tile of TILE rows:
-//   * the selected rows are gathered through the page table in (row, 64-column
-//     group) units: four 16-byte code loads plus one scale load per unit; FP8
-//     codes are dequantized in registers (exact E4M3 -> fp32, times the group
-//     scale, rounded to bf16) and written once to LDS as a row-major K tile
-//     (576 wide, swizzled against bank conflicts);
+//   * the selected rows are gathered through the page table in 16-byte chunks,
+//     the lanes of a wave instruction covering whole 128-byte lines; FP8 codes
+//     are dequantized in registers (exact E4M3 -> fp32, times the group scale,
+//     rounded to bf16) and written once to LDS as a row-major K tile (576
+//     wide, swizzled against bank conflicts);
 //   * the next tile's rows are prefetched into registers while the current
 //     tile is computed (gather loads are unconditional so nothing waits on them
 //     before the tile's stores);
 //   * S^T = K Q^T runs on the 16x16x32 bf16 MFMA with Q held in registers for
-//     the whole split; O += P V takes P straight from the S^T accumulators and
-//     reads V = K[:, :512] from the same LDS tile with the gfx950 transpose read
-//     (ds_read_b64_tr_b16), so no transposed copy is made;
-//   * the softmax keeps a per-head reference max in the log2 domain and only
-//     rescales O when a head's max grows by more than 2^8 (P stays <= 256, and
-//     the final normalisation is unaffected), so O is rarely touched.
-// Two layouts of the same scheme:
-//   * tiles of 32 and 64 rows: 8 waves, 2 per SIMD so the hardware interleaves
-//     LDS latency with MFMA work.  Waves w and w+4 own heads 16(w%4)..+16; each
-//     contracts one half of the 576 dims for S^T (half the Q registers) and the
-//     pair adds the two halves through LDS; both then run the same softmax and
-//     each accumulates one half of the 512 output columns;
+//     the whole split; O += P V reads V = K[:, :512] from the same LDS tile with
+//     the gfx950 transpose read (ds_read_b64_tr_b16), so no transposed copy is
+//     made.
+// Two layouts:
+//   * tiles of 32 and 64 rows (partial_v2_kernel): 8 waves, 2 per SIMD, each
+//     owning 32 heads, with a softmax whose per-head reference is fixed once
+//     (described at the kernel);
 //   * tiles of 128 rows (the K tile alone takes 148 KB of LDS): 4 waves, wave
-//     w owns heads 16w..+16 for all dims and columns.
+//     w owns heads 16w..+16 for all dims and columns, with a running reference
+//     max that rescales O only when it grows by more than 2^8.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -77,15 +73,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Staging units.  V unit u covers row v_row(u), latent columns 64*v_grp(u) ..+64;
-// rope unit u covers row r_row(u), rope columns 16*r_piece(u) ..+16.  Eight
-// consecutive lanes take eight consecutive rows, so their stores spread over
-// the banks.
-__device__ __forceinline__ int v_row(int u) { return (u & 7) | ((u >> 6) << 3); }
-__device__ __forceinline__ int v_grp(int u) { return (u >> 3) & 7; }
-__device__ __forceinline__ int r_row(int u) { return (u & 7) | ((u >> 5) << 3); }
-__device__ __forceinline__ int r_piece(int u) { return (u >> 3) & 3; }
-
 struct PartialArgs {
   const uint8_t* latent;
   int num_pages;
@@ -104,43 +91,45 @@ struct PartialArgs {
   float* lse_part;
 };
 
-// Register staging of NR rows of a tile, spread over NT threads.
+// Register staging of NR rows of a tile, spread over NT threads.  Chunk q of
+// the tile (16 bytes of a row) goes to thread q % NT, so the lanes of one
+// wave instruction read whole 128-byte lines of one or two rows.
 template <int KV, int NR, int NT>
 struct Stage;
 
-// FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.
+// FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.  Latent chunk
+// q (16 codes) is row q/32, columns 16(q%32)..+16, with the scale of group
+// (q%32)/4; rope chunk q is row q/4, rope columns 16(q%4)..+16.
 template <int NR, int NT>
 struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
   static constexpr int kStride = 640;
-  static constexpr int kVU = (NR * 8 + NT - 1) / NT;
-  static constexpr int kRU = (NR * 4 + NT - 1) / NT;
-  u32x4 vcode[kVU][4];
-  float vscale[kVU];
-  u32x4 rcode[kRU];
-  float rscale[kRU];
-  uint32_t vok, rok;   // bit i: unit i holds a valid row
+  static constexpr int kLC = (NR * 32 + NT - 1) / NT;
+  static constexpr int kRC = (NR * 4 + NT - 1) / NT;
+  u32x4 lcode[kLC];
+  float lscale[kLC];
+  u32x4 rcode[kRC];
+  float rscale[kRC];
+  uint32_t lok, rok;   // bit i: chunk i holds a valid row
 
   // Unconditional loads: invalid rows read row 0 and are zeroed when stored.
   __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int tid) {
-    vok = rok = 0;
+    lok = rok = 0;
 #pragma unroll
-    for (int i = 0; i < kVU; ++i) {
-      const int u = tid + NT * i;
-      const int phys = u < NR * 8 ? rows[v_row(u)] : -1;
-      vok |= uint32_t(phys >= 0) << i;
+    for (int i = 0; i < kLC; ++i) {
+      const int q = tid + NT * i;
+      const int phys = q < NR * 32 ? rows[q >> 5] : -1;
+      lok |= uint32_t(phys >= 0) << i;
       const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        vcode[i][m] = *reinterpret_cast<const u32x4*>(row + 64 * v_grp(u) + 16 * m);
-      vscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * v_grp(u));
+      lcode[i] = *reinterpret_cast<const u32x4*>(row + 16 * (q & 31));
+      lscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
     }
 #pragma unroll
-    for (int i = 0; i < kRU; ++i) {
-      const int u = tid + NT * i;
-      const int phys = u < NR * 4 ? rows[r_row(u)] : -1;
+    for (int i = 0; i < kRC; ++i) {
+      const int q = tid + NT * i;
+      const int phys = q < NR * 4 ? rows[q >> 2] : -1;
       rok |= uint32_t(phys >= 0) << i;
       const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
-      rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * r_piece(u));
+      rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (q & 3));
       rscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
     }
   }
@@ -162,97 +151,86 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
     *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = u32x4{b[4], b[5], b[6], b[7]};
   }
 
-  // rows are stored at r0 + (unit row)
+  // rows are stored at r0 + (tile row)
   __device__ __forceinline__ void store(uint16_t* k, int r0, int tid) const {
     const u32x4 z = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kVU; ++i) {
-      const int u = tid + NT * i;
-      const bool ok = (vok >> i) & 1u;
-      if (u < NR * 8) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          put16(k, r0 + v_row(u), 8 * v_grp(u) + 2 * m, ok ? vcode[i][m] : z, ok ? vscale[i] : 0.f);
-      }
+    for (int i = 0; i < kLC; ++i) {
+      const int q = tid + NT * i;
+      const bool ok = (lok >> i) & 1u;
+      if (q < NR * 32)
+        put16(k, r0 + (q >> 5), 2 * (q & 31), ok ? lcode[i] : z, ok ? lscale[i] : 0.f);
     }
 #pragma unroll
-    for (int i = 0; i < kRU; ++i) {
-      const int u = tid + NT * i;
+    for (int i = 0; i < kRC; ++i) {
+      const int q = tid + NT * i;
       const bool ok = (rok >> i) & 1u;
-      if (u < NR * 4)
-        put16(k, r0 + r_row(u), DSA_D_LATENT / 8 + 2 * r_piece(u), ok ? rcode[i] : z,
+      if (q < NR * 4)
+        put16(k, r0 + (q >> 2), DSA_D_LATENT / 8 + 2 * (q & 3), ok ? rcode[i] : z,
               ok ? rscale[i] : 0.f);
     }
   }
 };
 
-// BF16 rows: 576 bf16, stride 1152.
+// BF16 rows: 576 bf16, stride 1152.  Latent chunk q (8 values) is row q/64,
+// columns 8(q%64)..+8; rope chunk q is row q/8, rope columns 8(q%8)..+8.
 template <int NR, int NT>
 struct Stage<DSA_KV_BF16, NR, NT> {
   static constexpr int kStride = 2 * DSA_D_QK;
-  static constexpr int kVU = (NR * 8 + NT - 1) / NT;
-  static constexpr int kRU = (NR * 4 + NT - 1) / NT;
-  u32x4 vraw[kVU][8];
-  u32x4 rraw[kRU][2];
-  uint32_t vok, rok;
+  static constexpr int kLC = (NR * 64 + NT - 1) / NT;
+  static constexpr int kRC = (NR * 8 + NT - 1) / NT;
+  u32x4 lraw[kLC];
+  u32x4 rraw[kRC];
+  uint32_t lok, rok;
 
   __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int tid) {
-    vok = rok = 0;
+    lok = rok = 0;
 #pragma unroll
-    for (int i = 0; i < kVU; ++i) {
-      const int u = tid + NT * i;
-      const int phys = u < NR * 8 ? rows[v_row(u)] : -1;
-      vok |= uint32_t(phys >= 0) << i;
-      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        vraw[i][m] = *reinterpret_cast<const u32x4*>(row + 128 * v_grp(u) + 16 * m);
+    for (int i = 0; i < kLC; ++i) {
+      const int q = tid + NT * i;
+      const int phys = q < NR * 64 ? rows[q >> 6] : -1;
+      lok |= uint32_t(phys >= 0) << i;
+      lraw[i] = *reinterpret_cast<const u32x4*>(latent + int64_t(max(phys, 0)) * kStride +
+                                                16 * (q & 63));
     }
 #pragma unroll
-    for (int i = 0; i < kRU; ++i) {
-      const int u = tid + NT * i;
-      const int phys = u < NR * 4 ? rows[r_row(u)] : -1;
+    for (int i = 0; i < kRC; ++i) {
+      const int q = tid + NT * i;
+      const int phys = q < NR * 8 ? rows[q >> 3] : -1;
       rok |= uint32_t(phys >= 0) << i;
-      const u32x4* src = reinterpret_cast<const u32x4*>(latent + int64_t(max(phys, 0)) * kStride +
-                                                        2 * DSA_D_LATENT + 32 * r_piece(u));
-      rraw[i][0] = src[0];
-      rraw[i][1] = src[1];
+      rraw[i] = *reinterpret_cast<const u32x4*>(latent + int64_t(max(phys, 0)) * kStride +
+                                                2 * DSA_D_LATENT + 16 * (q & 7));
     }
   }
   __device__ __forceinline__ void store(uint16_t* k, int r0, int tid) const {
     const u32x4 z = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kVU; ++i) {
-      const int u = tid + NT * i;
-      const bool ok = (vok >> i) & 1u;
-      if (u < NR * 8) {
-#pragma unroll
-        for (int m = 0; m < 8; m += 2) {
-          const int r = r0 + v_row(u), sw = k_swz(r);
-          uint16_t* row = k + r * kKStride + 8 * (8 * v_grp(u) + m);
-          *reinterpret_cast<u32x4*>(row + 8 * sw) = ok ? vraw[i][m] : z;
-          *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = ok ? vraw[i][m + 1] : z;
-        }
+    for (int i = 0; i < kLC; ++i) {
+      const int q = tid + NT * i;
+      const bool ok = (lok >> i) & 1u;
+      if (q < NR * 64) {
+        const int r = r0 + (q >> 6);
+        *reinterpret_cast<u32x4*>(k + k_chunk_off(r, q & 63)) = ok ? lraw[i] : z;
       }
     }
 #pragma unroll
-    for (int i = 0; i < kRU; ++i) {
-      const int u = tid + NT * i;
+    for (int i = 0; i < kRC; ++i) {
+      const int q = tid + NT * i;
       const bool ok = (rok >> i) & 1u;
-      if (u < NR * 4) {
-        const int r = r0 + r_row(u), sw = k_swz(r);
-        uint16_t* row = k + r * kKStride + 8 * (DSA_D_LATENT / 8 + 2 * r_piece(u));
-        *reinterpret_cast<u32x4*>(row + 8 * sw) = ok ? rraw[i][0] : z;
-        *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = ok ? rraw[i][1] : z;
+      if (q < NR * 8) {
+        const int r = r0 + (q >> 3);
+        *reinterpret_cast<u32x4*>(k + k_chunk_off(r, DSA_D_LATENT / 8 + (q & 7))) = ok ? rraw[i] : z;
       }
     }
   }
 };
 
 // Physical rows (page*64 + slot, or -1 when masked) of index columns
-// [cc, cc + kRowChunk) of token t, written to rows[].
+// [cc, cc + kRowChunk) of token t, written to rows[]; with a bias array, also
+// 0 for a valid row and -inf for a masked one.
 __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int req, int pos, int cc,
-                                             int cend, int32_t* rows, int tid, int nthreads) {
+                                             int cend, int32_t* rows, int tid, int nthreads,
+                                             float* bias = nullptr) {
   for (int i = tid; i < kRowChunk; i += nthreads) {
     const int col = cc + i;
     int phys = -1;
@@ -268,6 +246,7 @@ __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int re
       }
     }
     rows[i] = phys;
+    if (bias) bias[i] = phys >= 0 ? 0.f : kNegInf;
   }
 }
 
@@ -292,8 +271,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB]
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sacc[mb][j]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = dsa::rows4_max(tmax);
   if (__any(tmax > m_ref + kRescaleThreshold)) {
     const float m_new = fmaxf(m_ref, tmax);
     const float alpha = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -322,13 +300,12 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB]
     pa[k2][half] = dsa::pack_bf16x2(p[0], p[1]);
     pa[k2][half + 1] = dsa::pack_bf16x2(p[2], p[3]);
   }
-  psum += __shfl_xor(psum, 16);
-  psum += __shfl_xor(psum, 32);
+  psum = dsa::rows4_sum(psum);
   l_run += psum;
 }
 
 // O[16 heads x kNB*16 columns from column col0] += P V over kKS*32 rows, V read
-// transposed from the K tile, two column blocks in flight.
+// transposed from the K tile.
 template <int kKS, int kNB>
 __device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS], f32x4 (&o)[kNB],
                                         int col0, int g, int c) {
@@ -336,6 +313,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS
   const int sw = (g ^ (g >> 1)) & 1;
   const uint16_t* vbase = k + (4 * g + (c >> 2)) * kKStride + col0 +
                           8 * ((((c & 3) >> 1)) ^ sw) + 4 * (c & 1);
+  // two column blocks in flight, their MFMAs alternating
 #pragma unroll
   for (int nb = 0; nb < kNB; nb += 2) {
     u32x4 vb[2][kKS];
@@ -384,122 +362,6 @@ __device__ __forceinline__ void scale_and_mask(f32x4 (&sacc)[kMB], const int32_t
         if (!((valid[r >> 6] >> (r & 63)) & 1ull)) sacc[mb][j] = kNegInf;
       }
   }
-}
-
-// ---------------------------------------------------------------------------
-// 8-wave kernel, tiles of 32 or 64 rows.
-constexpr int kThreads8 = 512;
-
-template <int TILE>
-struct Smem8 {
-  uint16_t k[TILE * kKStride];
-  int32_t rows[kRowChunk];
-  f32x4 xs[8][TILE / 16][64];      // partial S^T of each wave, lane-major
-};
-
-template <int KV, int TILE>
-__global__ __launch_bounds__(kThreads8) void partial8_kernel(PartialArgs a) {
-  static_assert(TILE == 32 || TILE == 64, "eight-wave layout covers tiles of 32 and 64 rows");
-  __shared__ __attribute__((aligned(16))) Smem8<TILE> sm;
-  constexpr int kMB = TILE / 16;
-  constexpr int kKS = TILE / 32;
-  constexpr int kQS = DSA_D_QK / 64;          // k-steps per half of the 576 dims (9)
-  constexpr int kNB = DSA_D_LATENT / 32;      // 16-column blocks per half of the 512 (16)
-
-  const int t = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = wave & 3, dh = wave >> 2;   // head group, half of the dims
-  const int g = lane >> 4, c = lane & 15;
-  const int c0 = s * a.cols_per_split;
-  const int c1 = min(a.width, c0 + a.cols_per_split);
-  const int req = request_of(a, t);
-  const int pos = a.tok_pos[t];
-
-  // Q of head 16hg + c, dims 288dh + 32ks + 8g .. +8 (MFMA B operand)
-  u32x4 qf[kQS];
-  {
-    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
-        a.q + (int64_t(t) * DSA_HEADS + 16 * hg + c) * DSA_D_QK + (DSA_D_QK / 2) * dh);
-#pragma unroll
-    for (int ks = 0; ks < kQS; ++ks) qf[ks] = qsrc[ks * 4 + g];
-  }
-  // Q must be resident before the tile loop, whose body would otherwise carry
-  // the wait for these loads into every iteration (behind the row prefetch).
-  __builtin_amdgcn_s_waitcnt(0);
-  f32x4 o[kNB];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf, l_run = 0.f;
-
-  // One tile's compute: partial S^T, pair exchange, softmax, P V.
-  auto compute_tile = [&](int it) {
-    f32x4 sacc[kMB];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // rows 16mb + c: swizzle bit fixed per lane; dims 288dh + 32ks + 8g
-    const uint16_t* kq = sm.k + c * kKStride + 8 * ((DSA_D_QK / 16) * dh + (g ^ k_swz(c)));
-#pragma unroll
-    for (int ks = 0; ks < kQS; ++ks) {
-      u32x4 kf[kMB];
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-        sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[ks]), sacc[mb]);
-    }
-    // S^T = half 0 + half 1, through LDS with the partner wave
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) sm.xs[wave][mb][lane] = sacc[mb];
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const f32x4 other = sm.xs[wave ^ 4][mb][lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)   // the same sum order on both waves of the pair
-        sacc[mb][j] = dh == 0 ? sacc[mb][j] + other[j] : other[j] + sacc[mb][j];
-    }
-    scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g, lane);
-    u32x4 pa[kKS];
-    softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
-    pv_tile<kKS, kNB>(sm.k, pa, o, (DSA_D_LATENT / 2) * dh, g, c);
-  };
-
-  // Row gathers run one tile ahead of the compute (a second register stage
-  // measured slower: it pushes the kernel into spills).
-  Stage<KV, TILE, kThreads8> st;
-  for (int cc = c0; cc < c1; cc += kRowChunk) {
-    const int cend = min(c1, cc + kRowChunk);
-    __syncthreads();
-    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads8);
-    __syncthreads();
-    const int ntile = (cend - cc + TILE - 1) / TILE;
-    st.load(a.latent, sm.rows, tid);
-    st.store(sm.k, 0, tid);
-    __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-      const bool more = it + 1 < ntile;
-      if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
-      compute_tile(it);
-      __syncthreads();
-      if (more) {
-        st.store(sm.k, 0, tid);
-        __syncthreads();
-      }
-    }
-  }
-
-  const int64_t ts = int64_t(t) * a.splits + s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lj = __shfl(l_run, 4 * g + j);
-    const float inv = lj > 0.f ? 1.f / lj : 0.f;
-    float* dst = a.o_part + (ts * DSA_HEADS + 16 * hg + 4 * g + j) * DSA_D_LATENT +
-                 (DSA_D_LATENT / 2) * dh + c;
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[nb][j] * inv;
-  }
-  if (g == 0 && dh == 0)
-    a.lse_part[ts * DSA_HEADS + 16 * hg + c] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -608,12 +470,250 @@ __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
     a.lse_part[ts * DSA_HEADS + 16 * wave + c] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave kernel with 32-head waves, tiles of 32 and 64 rows.  Wave w has
+// hp = w&1 (heads 32hp..+32), dh = (w>>1)&1 and rh = w>>2:
+//   * S^T: rows (TILE/2)rh..+TILE/2 of the tile, dims 288dh..+288, 32 heads -
+//     every K fragment read from LDS feeds two head blocks (half the reads of
+//     16-head waves) and Q of 32 heads x 288 dims stays in registers;
+//   * the dh pair swaps one head block of partial sums through LDS, so wave
+//     dh holds the whole S^T of head block dh on its rows and exponentiates
+//     only those (no softmax work is duplicated);
+//   * P goes to LDS in the PV operand's row order; wave w then accumulates
+//     O for its 32 heads on output columns 128(2rh+dh)..+128 over all rows
+//     of the tile (each V fragment read by transpose feeds two head blocks).
+// Softmax: the reference max of each head is fixed by the first tile with a
+// valid row (all heads at once: masking is per row), so O is never rescaled;
+// a tile sum above 2^52 (or not finite) sends the split through a second pass
+// whose reference is the exact max of the first.  Masked rows enter S^T as an
+// accumulator bias of -inf.
+constexpr int kThreadsV2 = 512;
+constexpr float kOverflowSum = 4503599627370496.f;   // 2^52
+
+template <int TILE>
+struct SmemV2 {
+  static constexpr int kPStride = TILE + 8;     // bf16 per head in the P buffer
+  uint16_t k[TILE * kKStride];
+  int32_t rows[kRowChunk];
+  float bias[kRowChunk];                        // 0 for a valid row, -inf for a masked one
+  f32x4 xs[8][TILE / 32][64];                   // partial S^T sent to the dh partner
+  uint16_t p[DSA_HEADS * kPStride];             // P[head][row in PV operand order]
+  float red[2][2][2][16];                       // [rh][hp][dh][head]: max / l partials
+};
+
+template <int KV, int TILE>
+__global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
+  static_assert(TILE == 32 || TILE == 64, "tiles of 32 and 64 rows");
+  __shared__ __attribute__((aligned(16))) SmemV2<TILE> sm;
+  constexpr int kPS = SmemV2<TILE>::kPStride;
+  constexpr int kOMB = TILE / 32;            // own 16-row blocks per wave
+  constexpr int kKS = TILE / 32;             // PV k-steps
+  constexpr int kQS = DSA_D_QK / 64;         // QK k-steps per half of the dims (9)
+  constexpr int kNB = DSA_D_LATENT / 64;     // 16-column blocks per quarter of the 512 (8)
+
+  const int t = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hp = wave & 1, dh = (wave >> 1) & 1, rh = wave >> 2;
+  const int cq = (wave >> 1) & 3;            // output column quarter (2rh + dh)
+  const int g = lane >> 4, c = lane & 15;
+  const int c0 = s * a.cols_per_split;
+  const int c1 = min(a.width, c0 + a.cols_per_split);
+  const int req = request_of(a, t);
+  const int pos = a.tok_pos[t];
+
+  // Q of heads 32hp + 16hb + c, dims 288dh + 32ks + 8g .. +8 (MFMA B operand)
+  u32x4 qf[2][kQS];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+        a.q + (int64_t(t) * DSA_HEADS + 32 * hp + 16 * hb + c) * DSA_D_QK + (DSA_D_QK / 2) * dh);
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks) qf[hb][ks] = qsrc[ks * 4 + g];
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // Q resident before the tile loop
+
+  f32x4 o[2][kNB];
+  float m_ref, l_run;               // head 32hp + 16dh + c (lane column c)
+  float m_run = kNegInf;            // exact running max over this wave's rows
+  bool overflow = false;
+  bool ref_set = false;             // workgroup-uniform: the references are fixed
+
+  // K operand: rows (TILE/2)rh + 16mb + c, dims 288dh + 32ks + 8g
+  const int klane = ((TILE / 2) * rh + c) * kKStride + 8 * ((DSA_D_QK / 16) * dh + (g ^ k_swz(c)));
+  // V transpose read: rows 32k2 + 4g + c/4 (+16), columns 128cq + 16nb
+  const int vsw = (g ^ (g >> 1)) & 1;
+  const int vlane = (4 * g + (c >> 2)) * kKStride + (DSA_D_LATENT / 4) * cq +
+                    8 * (((c & 3) >> 1) ^ vsw) + 4 * (c & 1);
+  // P: written at head 32hp + 16dh + c, read as the A operand of head 32hp + 16hb + c
+  uint16_t* pw = sm.p + (32 * hp + 16 * dh + c) * kPS;
+
+  auto compute_tile = [&](int it, const uint16_t* kt) {
+    // S^T over this wave's rows and half of the dims, starting at the row bias
+    f32x4 sacc[kOMB][2];
+#pragma unroll
+    for (int mb = 0; mb < kOMB; ++mb) {
+      const f32x4 b =
+          *reinterpret_cast<const f32x4*>(sm.bias + it * TILE + (TILE / 2) * rh + 16 * mb + 4 * g);
+      sacc[mb][0] = b;
+      sacc[mb][1] = b;
+    }
+    const uint16_t* kq = kt + klane;
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks) {
+      u32x4 kf[kOMB];
+#pragma unroll
+      for (int mb = 0; mb < kOMB; ++mb)
+        kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
+#pragma unroll
+      for (int mb = 0; mb < kOMB; ++mb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
+                                           sacc[mb][hb]);
+    }
+    // keep head block dh, send head block 1-dh to the partner (wave ^ 2)
+    f32x4 sv[kOMB];
+#pragma unroll
+    for (int mb = 0; mb < kOMB; ++mb) {
+      sm.xs[wave][mb][lane] = dh ? sacc[mb][0] : sacc[mb][1];
+      sv[mb] = dh ? sacc[mb][1] : sacc[mb][0];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < kOMB; ++mb) sv[mb] += sm.xs[wave ^ 2][mb][lane];   // float + commutes
+
+    // tile max of the head over this wave's rows (log2 units, scale > 0)
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < kOMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sv[mb][j]);
+    tmax = dsa::rows4_max(tmax) * a.scale_log2;
+    m_run = fmaxf(m_run, tmax);
+    // the first tile with a valid row fixes every head's reference (the
+    // condition reads only shared row data, so all waves take the branch)
+    if (!ref_set &&
+        __ballot(lane < TILE && sm.rows[it * TILE + min(lane, TILE - 1)] >= 0) != 0ull) {
+      if (g == 0) sm.red[rh][hp][dh][c] = tmax;
+      __syncthreads();
+      m_ref = fmaxf(sm.red[0][hp][dh][c], sm.red[1][hp][dh][c]);
+      __syncthreads();
+      ref_set = true;
+    }
+    const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kOMB; ++mb) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(fmaf(sv[mb][j], a.scale_log2, neg_m));   // exp2(-inf) = 0
+        psum += p[j];
+      }
+      // rows (TILE/2)rh + 16mb + 4g + j -> position 32k2 + 8g + 4h + j
+      const int blk = kOMB * rh + mb;
+      *reinterpret_cast<u32x2*>(pw + 32 * (blk >> 1) + 8 * g + 4 * (blk & 1)) =
+          u32x2{dsa::pack_bf16x2(p[0], p[1]), dsa::pack_bf16x2(p[2], p[3])};
+    }
+    psum = dsa::rows4_sum(psum);
+    l_run += psum;
+    overflow = overflow || !(psum <= kOverflowSum);
+    __syncthreads();
+
+    // O[32 heads x 128 columns] += P V over the tile's rows
+    u32x4 pa[2][kKS];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int k2 = 0; k2 < kKS; ++k2)
+        pa[hb][k2] = *reinterpret_cast<const u32x4*>(sm.p + (32 * hp + 16 * hb + c) * kPS + 32 * k2 + 8 * g);
+    const uint16_t* vb0 = kt + vlane;
+#pragma unroll
+    for (int k2 = 0; k2 < kKS; ++k2)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const uint16_t* vp = vb0 + 32 * k2 * kKStride + 16 * nb;
+        const u32x2 lo2 = lds_read_tr16(vp);
+        const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
+        const u32x4 vb = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          o[hb][nb] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[hb][k2]), dsa::as_bf16x8(vb), o[hb][nb]);
+      }
+  };
+
+  Stage<KV, TILE, kThreadsV2> st;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    if (pass == 0) {
+      m_ref = kNegInf;
+      ref_set = false;
+    } else {
+      // exact max of the first pass, over both row halves
+      if (g == 0) sm.red[rh][hp][dh][c] = m_run;
+      __syncthreads();
+      m_ref = fmaxf(sm.red[0][hp][dh][c], sm.red[1][hp][dh][c]);
+      overflow = false;
+      ref_set = true;
+    }
+    for (int cc = c0; cc < c1; cc += kRowChunk) {
+      const int cend = min(c1, cc + kRowChunk);
+      __syncthreads();
+      resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, sm.bias);
+      __syncthreads();
+      const int ntile = (cend - cc + TILE - 1) / TILE;
+      st.load(a.latent, sm.rows, tid);
+      st.store(sm.k, 0, tid);
+      __syncthreads();
+      for (int it = 0; it < ntile; ++it) {
+        const bool more = it + 1 < ntile;
+        if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
+        compute_tile(it, sm.k);
+        __syncthreads();
+        if (more) {
+          st.store(sm.k, 0, tid);
+          __syncthreads();
+        }
+      }
+    }
+    if (!__syncthreads_or(overflow)) break;
+  }
+
+  // l of each head = the two row halves' sums; then normalize and write
+  __syncthreads();
+  if (g == 0) sm.red[rh][hp][dh][c] = l_run;
+  __syncthreads();
+  const int64_t ts = int64_t(t) * a.splits + s;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * g + j;
+      const float lj = sm.red[0][hp][hb][hh] + sm.red[1][hp][hb][hh];
+      const float inv = lj > 0.f ? 1.f / lj : 0.f;
+      float* dst = a.o_part + (ts * DSA_HEADS + 32 * hp + 16 * hb + hh) * DSA_D_LATENT +
+                   (DSA_D_LATENT / 4) * cq + c;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[hb][nb][j] * inv;
+    }
+  }
+  if (rh == 0 && g == 0) {
+    const float l = sm.red[0][hp][dh][c] + sm.red[1][hp][dh][c];
+    a.lse_part[ts * DSA_HEADS + 32 * hp + 16 * dh + c] =
+        l > 0.f ? (m_ref + log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
 template <int KV, int TILE>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
   if constexpr (TILE == kTile4)
     hipLaunchKernelGGL((partial4_kernel<KV>), dim3(T, S), dim3(kThreads4), 0, st, a);
   else
-    hipLaunchKernelGGL((partial8_kernel<KV, TILE>), dim3(T, S), dim3(kThreads8), 0, st, a);
+    hipLaunchKernelGGL((partial_v2_kernel<KV, TILE>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   return hipGetLastError();
 }
 
@@ -669,8 +769,8 @@ extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: kv_tile must be 32, 64 or 128");
   if (num_splits < 1 || num_splits > 65535)
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: num_splits must be in [1, 65535]");
-  if (!std::isfinite(sm_scale))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: sm_scale must be finite and > 0");
   if (num_tokens == 0) return dsa::ok();
   if (!q || !idx || !o_part || !lse_part)
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: q, idx, o_part, lse_part must be non-null");

@@ -104,6 +104,43 @@ def test_partial_peaked_softmax_and_single_rows():
             check_attention(out_h[t], lse_h[t], ref["o"], ref["lse"], f"token {t}")
 
 
+def test_partial_later_tile_far_above_first_tile():
+    # One row of request 1 gets a score about 200 (natural units, sm_scale 1)
+    # above everything in the first tile of the index: at tile 32 the kernel's
+    # reference max, fixed by the first tile, is far too low, and the split
+    # must be recomputed with the exact max.  At tile 64 the row is in the
+    # first tile.  Both must match the oracle.
+    wl = synth.generate(synth.spec("tiny_bf16"), seed=7, device="cpu")
+    b, t, p_hi = 1, 3, 120
+    assert int(wl.tok_req[t]) == b and int(wl.tok_pos[t]) >= 131
+    q = O.bf16_bits_to_f64(wl.q[t].view(torch.uint16).numpy())          # [64, 576]
+    v = q.sum(axis=0)
+    assert (q @ v).min() > 0
+    k_hi = v * (250.0 / (q @ v).min())
+    bits = torch.from_numpy(k_hi.astype(np.float32)).to(torch.bfloat16).view(torch.uint8)
+    phys = int(wl.page_table[b, p_hi // 64]) * 64 + p_hi % 64
+    stride = synth.ROW_STRIDE[wl.spec.kv_dtype]
+    wl.pool[phys * stride: phys * stride + 2 * 576] = bits
+    wl = wl.to(DEV)
+    hv = HostView(wl)
+    hv.sm_scale = 1.0
+    cols = np.concatenate([np.arange(32), np.arange(100, 132)]).astype(np.int32)
+    idx = torch.from_numpy(np.tile(cols, (wl.num_tokens, 1))).to(DEV)
+    pool = make_pool(wl)
+    for tile in (32, 64):
+        say(f"[case] partial tile={tile}: dominant row in the second half of the index")
+        o_p, lse_p = dsa.sparse_mla_partial(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q,
+                                            idx, 1.0, tile, 1)
+        out, lse = dsa.combine(o_p, lse_p)
+        torch.cuda.synchronize()
+        out_h, lse_h = bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+        for tt in range(wl.num_tokens):
+            ref = hv.token(tt, tile, 1, idx=cols)
+            check_attention(out_h[tt], lse_h[tt], ref["o"], ref["lse"], f"tile {tile} token {tt}")
+            if tt == t:   # the case is what it claims: every head's max is the planted row
+                assert np.all(ref["lse"] > 200)
+
+
 def test_all_masked_token_gives_zero_and_neg_inf():
     wl = _gen("tiny_fp8", seed=4)
     pool = make_pool(wl)
