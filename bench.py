@@ -26,27 +26,32 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
 
 
-def algorithmic_bytes(spec, plan, kv_row_bytes):
-    """Bytes each kernel must move at minimum, per launch (one step)."""
+def algorithmic_bytes(spec, plan, kv_row_bytes, fused=False):
+    """Bytes each kernel must move at minimum, per launch (one step).  With one
+    split (fused) Partial writes the bf16 output and lse itself; no Combine."""
     T = spec.num_tokens
     k = spec.k
     S = plan.splits
+    out_bytes = T * 64 * (512 * 2 + 4)
     keys = 0
     for L, q in zip(spec.ctx_lens, spec.q_per_req):
         # a request's visible keys are read once for all its query tokens
         keys += L * 256
     vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
               for p in range(L - q, L))
-    return {
+    d = {
         # keys + indexer queries/weights + visible score writes
         "index_scores": keys + T * (16 * 128 * 2 + 16 * 4) + vis * 4,
         # visible score reads + index writes
         "topk": vis * 4 + T * k * 4,
-        # index reads + selected latent rows + q + split partials
-        "partial": T * k * 4 + T * k * kv_row_bytes + T * 64 * 576 * 2 + T * S * 64 * (512 + 1) * 4,
-        # split partials in, bf16 output + lse out
-        "combine": T * S * 64 * (512 + 1) * 4 + T * 64 * (512 * 2 + 4),
     }
+    attend_in = T * k * 4 + T * k * kv_row_bytes + T * 64 * 576 * 2   # index, selected rows, q
+    if fused:
+        d["partial"] = attend_in + out_bytes
+    else:
+        d["partial"] = attend_in + T * S * 64 * (512 + 1) * 4          # split partials out
+        d["combine"] = T * S * 64 * (512 + 1) * 4 + out_bytes          # split partials in
+    return d
 
 
 def flops(spec):
@@ -253,12 +258,16 @@ def main():
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     # per-kernel timing on the same stream (separate loop, events between calls)
-    names = ["index_scores", "topk", "partial", "combine"]
-    calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk, lambda: path.partial(wl.q),
-             path.combine]
+    if path.fused:
+        names = ["index_scores", "topk", "partial"]
+        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk, lambda: path.attend(wl.q)]
+    else:
+        names = ["index_scores", "topk", "partial", "combine"]
+        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk,
+                 lambda: path.partial(wl.q), path.combine]
     acc = {n: 0.0 for n in names}
     for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         evs[0].record(stream)
         for i, c in enumerate(calls):
             c()
@@ -269,7 +278,7 @@ def main():
     per_us = {n: 1000.0 * acc[n] / args.steps for n in names}
 
     lay = dsa.pool_layout(spec.kv_dtype, 1)
-    byts = algorithmic_bytes(spec, plan, lay.latent_row_bytes)
+    byts = algorithmic_bytes(spec, plan, lay.latent_row_bytes, path.fused)
     fl = flops(spec)
     kernels = {}
     for n in names:
@@ -298,7 +307,8 @@ def main():
         "config": {"workload": spec.name, "requests": spec.num_reqs, "query_tokens": T,
                    "context": int(max(spec.ctx_lens)), "top_k": spec.k, "heads": 64,
                    "kv": "fp8_e4m3_s64" if spec.kv_dtype == dsa.KV_FP8 else "bf16",
-                   "kv_tile": plan.tile, "splits": plan.splits},
+                   "kv_tile": plan.tile, "splits": plan.splits,
+                   "combine": "in partial (one split)" if path.fused else "separate kernel"},
         "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
                 "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
         "kernels": kernels,

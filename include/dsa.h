@@ -213,6 +213,20 @@ dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t* page_tabl
                                   int32_t kv_tile, int32_t num_splits, float* o_part,
                                   float* lse_part, void* stream);
 
+/* Sparse MLA in one pass over each token's index row [LMSYS-3: with a single
+ * split there are no intermediates and no Combine work]: the same attention
+ * as dsa_sparse_mla_partial with num_splits = 1 followed by dsa_combine, and
+ * bit for bit the same result (Combine of one split multiplies by exp(0) = 1
+ * and adds log 1 = 0), without the fp32 intermediates.  Same arguments and
+ * errors as dsa_sparse_mla_partial; kv_tile in {32, 64, 128}.
+ * out: bf16 [num_tokens,64,512]; lse: fp32 [num_tokens,64] (natural log).
+ * q 16-byte aligned; out, lse 4-byte aligned. */
+dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                          const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
+                          int32_t num_tokens, const uint16_t* q, const int32_t* idx,
+                          int32_t width, float sm_scale, int32_t kv_tile, uint16_t* out,
+                          float* lse, void* stream);
+
 /* Combine [LMSYS-3]: per token and head,
  *   lse = ln sum_s exp(lse_part_s),  out = sum_s exp(lse_part_s - lse) * o_part_s
  * with splits whose lse is -inf contributing nothing (all -inf: out = 0,

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -89,7 +90,27 @@ struct PartialArgs {
   int splits;
   float* o_part;
   float* lse_part;
+  uint16_t* out;         // single-split form: final bf16 output [T,64,512]
+  float* lse_out;        // and its lse [T,64]
 };
+
+// Output of one (token, split, head, column) value.  With kFinal (one split,
+// no Combine) the normalized value is written in bf16 to the final output;
+// that is bit for bit what Combine makes of a single split (weight exp(0) = 1).
+template <bool kFinal>
+__device__ __forceinline__ void put_out(const PartialArgs& a, int64_t ts, int head, int col, float v) {
+  if constexpr (kFinal)
+    a.out[(ts * DSA_HEADS + head) * DSA_D_LATENT + col] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  else
+    a.o_part[(ts * DSA_HEADS + head) * DSA_D_LATENT + col] = v;
+}
+template <bool kFinal>
+__device__ __forceinline__ void put_lse(const PartialArgs& a, int64_t ts, int head, float v) {
+  if constexpr (kFinal)
+    a.lse_out[ts * DSA_HEADS + head] = v;
+  else
+    a.lse_part[ts * DSA_HEADS + head] = v;
+}
 
 // Register staging of NR rows of a tile, spread over NT threads.  Chunk q of
 // the tile (16 bytes of a row) goes to thread q % NT, so the lanes of one
@@ -381,7 +402,7 @@ constexpr int prefetch_rows4() {
   return KV == DSA_KV_BF16 ? 64 : kTile4;
 }
 
-template <int KV>
+template <int KV, bool kFinal>
 __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) Smem4 sm;
   constexpr int TILE = kTile4;
@@ -462,12 +483,11 @@ __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
   for (int j = 0; j < 4; ++j) {
     const float lj = __shfl(l_run, 4 * g + j);
     const float inv = lj > 0.f ? 1.f / lj : 0.f;
-    float* dst = a.o_part + (ts * DSA_HEADS + 16 * wave + 4 * g + j) * DSA_D_LATENT + c;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[nb][j] * inv;
+    for (int nb = 0; nb < kNB; ++nb) put_out<kFinal>(a, ts, 16 * wave + 4 * g + j, 16 * nb + c, o[nb][j] * inv);
   }
   if (g == 0)
-    a.lse_part[ts * DSA_HEADS + 16 * wave + c] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
+    put_lse<kFinal>(a, ts, 16 * wave + c, l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf);
 }
 
 // ---------------------------------------------------------------------------
@@ -501,7 +521,7 @@ struct SmemV2 {
   float red[2][2][2][16];                       // [rh][hp][dh][head]: max / l partials
 };
 
-template <int KV, int TILE>
+template <int KV, int TILE, bool kFinal>
 __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   static_assert(TILE == 32 || TILE == 64, "tiles of 32 and 64 rows");
   __shared__ __attribute__((aligned(16))) SmemV2<TILE> sm;
@@ -695,25 +715,24 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       const int hh = 4 * g + j;
       const float lj = sm.red[0][hp][hb][hh] + sm.red[1][hp][hb][hh];
       const float inv = lj > 0.f ? 1.f / lj : 0.f;
-      float* dst = a.o_part + (ts * DSA_HEADS + 32 * hp + 16 * hb + hh) * DSA_D_LATENT +
-                   (DSA_D_LATENT / 4) * cq + c;
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = o[hb][nb][j] * inv;
+      for (int nb = 0; nb < kNB; ++nb)
+        put_out<kFinal>(a, ts, 32 * hp + 16 * hb + hh, (DSA_D_LATENT / 4) * cq + 16 * nb + c,
+                        o[hb][nb][j] * inv);
     }
   }
   if (rh == 0 && g == 0) {
     const float l = sm.red[0][hp][dh][c] + sm.red[1][hp][dh][c];
-    a.lse_part[ts * DSA_HEADS + 32 * hp + 16 * dh + c] =
-        l > 0.f ? (m_ref + log2f(l)) * kLn2 : kNegInf;
+    put_lse<kFinal>(a, ts, 32 * hp + 16 * dh + c, l > 0.f ? (m_ref + log2f(l)) * kLn2 : kNegInf);
   }
 }
 
-template <int KV, int TILE>
+template <int KV, int TILE, bool kFinal>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
   if constexpr (TILE == kTile4)
-    hipLaunchKernelGGL((partial4_kernel<KV>), dim3(T, S), dim3(kThreads4), 0, st, a);
+    hipLaunchKernelGGL((partial4_kernel<KV, kFinal>), dim3(T, S), dim3(kThreads4), 0, st, a);
   else
-    hipLaunchKernelGGL((partial_v2_kernel<KV, TILE>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
+    hipLaunchKernelGGL((partial_v2_kernel<KV, TILE, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   return hipGetLastError();
 }
 
@@ -754,29 +773,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t* page_table,
-                                             int32_t pt_stride, const int32_t* q_offsets,
-                                             int32_t num_reqs, const int32_t* tok_pos,
-                                             int32_t num_tokens, const uint16_t* q,
-                                             const int32_t* idx, int32_t width, float sm_scale,
-                                             int32_t kv_tile, int32_t num_splits, float* o_part,
-                                             float* lse_part, void* stream) {
+// Validation and launch shared by the split form (o_part/lse_part) and the
+// single-split form (out/lse).  `who` names the entry point in messages.
+static dsa_status run_partial(const char* who, const dsa_pool* pool, const int32_t* page_table,
+                              int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                              const int32_t* tok_pos, int32_t num_tokens, const uint16_t* q,
+                              const int32_t* idx, int32_t width, float sm_scale, int32_t kv_tile,
+                              int32_t num_splits, float* o_part, float* lse_part, uint16_t* out,
+                              float* lse_out, void* stream) {
+  const std::string w(who);
   dsa_status s = dsa::check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
-                                  num_tokens, "dsa_sparse_mla_partial");
+                                  num_tokens, who);
   if (s != DSA_OK) return s;
-  if (width < 1) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: width must be >= 1");
+  if (width < 1) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": width must be >= 1");
   if (kv_tile != 32 && kv_tile != 64 && kv_tile != 128)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: kv_tile must be 32, 64 or 128");
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": kv_tile must be 32, 64 or 128");
   if (num_splits < 1 || num_splits > 65535)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: num_splits must be in [1, 65535]");
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": num_splits must be in [1, 65535]");
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: sm_scale must be finite and > 0");
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": sm_scale must be finite and > 0");
   if (num_tokens == 0) return dsa::ok();
-  if (!q || !idx || !o_part || !lse_part)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: q, idx, o_part, lse_part must be non-null");
-  if (!dsa::aligned(q, 16) || !dsa::aligned(idx, 4) || !dsa::aligned(o_part, 16) ||
-      !dsa::aligned(lse_part, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_sparse_mla_partial: q and o_part must be 16-byte aligned");
+  const bool final_out = num_splits == 1 && (out != nullptr || lse_out != nullptr);
+  if (!q || !idx || (final_out ? (!out || !lse_out) : (!o_part || !lse_part)))
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": q, idx and the outputs must be non-null");
+  if (!dsa::aligned(q, 16) || !dsa::aligned(idx, 4) ||
+      (final_out ? !dsa::aligned(out, 4) || !dsa::aligned(lse_out, 4)
+                 : !dsa::aligned(o_part, 16) || !dsa::aligned(lse_part, 4)))
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": q must be 16-byte aligned, o_part 16-byte, "
+                                              "out/lse 4-byte");
   dsa_partial_plan plan;
   if (dsa_plan_partial(num_tokens, width, kv_tile, num_splits, 0, &plan) != DSA_OK)
     return DSA_ERR_INVALID_ARG;
@@ -796,22 +820,54 @@ extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t
   a.splits = num_splits;
   a.o_part = o_part;
   a.lse_part = lse_part;
+  a.out = out;
+  a.lse_out = lse_out;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
   const bool fp8 = pool->kv_dtype == DSA_KV_FP8_E4M3_S64;
-  if (kv_tile == 32)
-    e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 32>(a, num_tokens, num_splits, st)
-            : launch_partial<DSA_KV_BF16, 32>(a, num_tokens, num_splits, st);
-  else if (kv_tile == 64)
-    e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 64>(a, num_tokens, num_splits, st)
-            : launch_partial<DSA_KV_BF16, 64>(a, num_tokens, num_splits, st);
-  else
-    e = fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, 128>(a, num_tokens, num_splits, st)
-            : launch_partial<DSA_KV_BF16, 128>(a, num_tokens, num_splits, st);
+  auto launch = [&](auto tile_c, auto final_c) -> hipError_t {
+    constexpr int TILE = decltype(tile_c)::value;
+    constexpr bool FIN = decltype(final_c)::value;
+    return fp8 ? launch_partial<DSA_KV_FP8_E4M3_S64, TILE, FIN>(a, num_tokens, num_splits, st)
+               : launch_partial<DSA_KV_BF16, TILE, FIN>(a, num_tokens, num_splits, st);
+  };
+  using T32 = std::integral_constant<int, 32>;
+  using T64 = std::integral_constant<int, 64>;
+  using T128 = std::integral_constant<int, 128>;
+  hipError_t e;
+  if (final_out) {
+    if (kv_tile == 32) e = launch(T32{}, std::true_type{});
+    else if (kv_tile == 64) e = launch(T64{}, std::true_type{});
+    else e = launch(T128{}, std::true_type{});
+  } else {
+    if (kv_tile == 32) e = launch(T32{}, std::false_type{});
+    else if (kv_tile == 64) e = launch(T64{}, std::false_type{});
+    else e = launch(T128{}, std::false_type{});
+  }
   if (e != hipSuccess)
-    return dsa::fail(DSA_ERR_HIP, std::string("dsa_sparse_mla_partial: launch failed: ") +
-                                      hipGetErrorString(e));
+    return dsa::fail(DSA_ERR_HIP, w + ": launch failed: " + hipGetErrorString(e));
   return dsa::ok();
+}
+
+extern "C" dsa_status dsa_sparse_mla_partial(const dsa_pool* pool, const int32_t* page_table,
+                                             int32_t pt_stride, const int32_t* q_offsets,
+                                             int32_t num_reqs, const int32_t* tok_pos,
+                                             int32_t num_tokens, const uint16_t* q,
+                                             const int32_t* idx, int32_t width, float sm_scale,
+                                             int32_t kv_tile, int32_t num_splits, float* o_part,
+                                             float* lse_part, void* stream) {
+  return run_partial("dsa_sparse_mla_partial", pool, page_table, pt_stride, q_offsets, num_reqs,
+                     tok_pos, num_tokens, q, idx, width, sm_scale, kv_tile, num_splits, o_part,
+                     lse_part, nullptr, nullptr, stream);
+}
+
+extern "C" dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_table,
+                                     int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                                     const int32_t* tok_pos, int32_t num_tokens, const uint16_t* q,
+                                     const int32_t* idx, int32_t width, float sm_scale,
+                                     int32_t kv_tile, uint16_t* out, float* lse, void* stream) {
+  return run_partial("dsa_sparse_mla", pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
+                     num_tokens, q, idx, width, sm_scale, kv_tile, 1, nullptr, nullptr, out, lse,
+                     stream);
 }
 
 extern "C" dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,

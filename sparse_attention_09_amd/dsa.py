@@ -38,7 +38,7 @@ EXPORTS = [
     "dsa_pool_share", "dsa_pool_release", "dsa_pool_free_pages", "dsa_pool_refcount",
     "dsa_pool_num_pages", "dsa_pool_kv_dtype",
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
-    "dsa_sparse_mla_partial", "dsa_combine",
+    "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine",
 ]
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "dsa_plan_partial": (i32, [i32, i32, i32, i32, i32, ctypes.POINTER(PartialPlan)]),
             "dsa_sparse_mla_partial": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32,
                                              i32, vp, vp, vp]),
+            "dsa_sparse_mla": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32, vp, vp,
+                                     vp]),
             "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -280,6 +282,30 @@ def sparse_mla_partial(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_sc
     return o_part, lse_part
 
 
+def sparse_mla(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_scale: float, kv_tile: int,
+               out=None, lse=None):
+    """Single-split sparse MLA straight to the bf16 output and lse (no Combine)."""
+    dev = pool.device
+    T = tok_pos.numel()
+    B = q_offsets.numel() - 1
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(q, "q", torch.bfloat16, dev, (T, HEADS, D_QK))
+    _need(idx, "idx", torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (T, HEADS, D_LATENT))
+    _need(lse, "lse", torch.float32, dev, (T, HEADS))
+    _check(lib().dsa_sparse_mla(pool.handle, _ptr(page_table), page_table.shape[-1],
+                                _ptr(q_offsets), B, _ptr(tok_pos), T, _ptr(q), _ptr(idx),
+                                idx.shape[-1], float(sm_scale), kv_tile, _ptr(out), _ptr(lse),
+                                _stream(dev)))
+    return out, lse
+
+
 def combine(o_part: torch.Tensor, lse_part: torch.Tensor, out=None, lse=None):
     dev = o_part.device
     _need(o_part, "o_part", torch.float32, dev)
@@ -301,8 +327,10 @@ def default_sm_scale() -> float:
 
 
 class DsaPath:
-    """The four calls of one decode/prefill step, with their buffers allocated
-    once for a fixed batch shape (so repeated steps allocate nothing)."""
+    """The calls of one decode/prefill step, with their buffers allocated once
+    for a fixed batch shape (so repeated steps allocate nothing).  With one
+    KV split the attention runs as dsa_sparse_mla (final output directly, no
+    Combine); with several, as dsa_sparse_mla_partial + dsa_combine."""
 
     def __init__(self, pool: Pool, page_table, q_offsets, tok_pos, max_q: int, max_ctx: int,
                  k: int, kv_tile: int = 0, num_splits: int = 0, sm_scale: Optional[float] = None,
@@ -321,8 +349,10 @@ class DsaPath:
         need = topk_workspace_bytes(T, max_ctx, k)
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
         S = self.plan.splits
-        self.o_part = torch.empty((T, S, HEADS, D_LATENT), dtype=torch.float32, device=dev)
-        self.lse_part = torch.empty((T, S, HEADS), dtype=torch.float32, device=dev)
+        self.fused = S == 1
+        self.o_part = self.lse_part = None
+        if not self.fused:
+            self._alloc_parts()
         self.out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
 
@@ -333,7 +363,15 @@ class DsaPath:
     def topk(self):
         return topk(self.scores, self.tok_pos, self.k, self.max_ctx, self.idx, self.workspace)
 
+    def _alloc_parts(self):
+        T, S, dev = self.T, self.plan.splits, self.pool.device
+        self.o_part = torch.empty((T, S, HEADS, D_LATENT), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((T, S, HEADS), dtype=torch.float32, device=dev)
+
     def partial(self, q):
+        """Split form (intermediates allocated on first use for a one-split plan)."""
+        if self.o_part is None:
+            self._alloc_parts()
         return sparse_mla_partial(self.pool, self.page_table, self.q_offsets, self.tok_pos, q,
                                   self.idx, self.sm_scale, self.plan.tile, self.plan.splits,
                                   self.o_part, self.lse_part)
@@ -341,8 +379,14 @@ class DsaPath:
     def combine(self):
         return combine(self.o_part, self.lse_part, self.out, self.lse)
 
+    def attend(self, q):
+        if self.fused:
+            return sparse_mla(self.pool, self.page_table, self.q_offsets, self.tok_pos, q,
+                              self.idx, self.sm_scale, self.plan.tile, self.out, self.lse)
+        self.partial(q)
+        return self.combine()
+
     def step(self, q_idx, w, q):
         self.index_scores(q_idx, w)
         self.topk()
-        self.partial(q)
-        return self.combine()
+        return self.attend(q)

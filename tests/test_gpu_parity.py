@@ -141,6 +141,25 @@ def test_partial_later_tile_far_above_first_tile():
                 assert np.all(ref["lse"] > 200)
 
 
+@pytest.mark.parametrize("name", ["tiny_fp8", "tiny_bf16"])
+def test_single_split_call_equals_partial_plus_combine(name):
+    # dsa_sparse_mla (final output, no Combine) against the split form with one
+    # split followed by Combine: bit for bit, at every tile size
+    wl = _gen(name, seed=6)
+    pool = make_pool(wl)
+    idx = synth.random_index(wl.tok_pos, 300, seed=66, frac_invalid=0.1).to(DEV)
+    for tile in (32, 64, 128):
+        say(f"[case] single-split form {name} tile={tile}")
+        o_p, lse_p = dsa.sparse_mla_partial(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q, idx,
+                                            wl.spec.sm_scale, tile, 1)
+        out_a, lse_a = dsa.combine(o_p, lse_p)
+        out_b, lse_b = dsa.sparse_mla(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q, idx,
+                                      wl.spec.sm_scale, tile)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+        assert torch.equal(lse_a, lse_b)
+
+
 def test_all_masked_token_gives_zero_and_neg_inf():
     wl = _gen("tiny_fp8", seed=4)
     pool = make_pool(wl)

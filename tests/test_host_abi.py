@@ -214,6 +214,17 @@ def test_compute_calls_validate_before_launch():
                                     None) == 1
     assert L.dsa_sparse_mla_partial(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(float("nan")), 64,
                                     1, f, f, None) == 1
+    assert L.dsa_sparse_mla_partial(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(-0.1), 64,
+                                    1, f, f, None) == 1
+    assert L.dsa_sparse_mla_partial(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(0.1), 64,
+                                    1, None, f, None) == 1
+    # single-split form: same checks, outputs required
+    assert L.dsa_sparse_mla(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(0.1), 48, f, f, None) == 1
+    assert L.dsa_sparse_mla(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(0.0), 64, f, f, None) == 1
+    assert L.dsa_sparse_mla(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(0.1), 64, None, f, None) == 1
+    assert L.dsa_sparse_mla(h, f, 4, f, 1, f, 1, f, f, 64, ctypes.c_float(0.1), 64, f, None, None) == 1
+    assert L.dsa_sparse_mla(h, f, 4, f, 1, f, 0, None, None, 64, ctypes.c_float(0.1), 64, None, None,
+                            None) == 0
     # combine
     assert L.dsa_combine(f, f, 1, 0, f, f, None) == 1
     assert L.dsa_combine(None, f, 1, 1, f, f, None) == 1
