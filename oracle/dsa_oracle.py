@@ -35,7 +35,14 @@ silent (each is listed with its reason in the design notes of the repository):
     c = tile * ceil(ceil(W/tile)/S); an empty split yields (o=0, lse=-inf);
   * combine:  lse = logsumexp_s lse_s,  o = sum_s exp(lse_s - lse) * o_s;
   * FP8 rows: 576 OCP E4M3FN codes followed by nine little-endian fp32 scales,
-    one per 64 consecutive elements; value = decode(code) * scale.
+    one per 64 consecutive elements; value = decode(code) * scale;
+  * writing a new token into the cache (SGLang cookbook: FP8 KV cache by
+    default; the quantizer itself is not spelled out): per group of 64,
+    scale = amax / 448 in fp32 (1 if the group is all zero) and
+    code = E4M3FN(x / scale), rounded to the nearest finite value with ties to
+    the even code, saturating at 448; the row's 28 pad bytes are zero.  The
+    scale and x / scale are formed in fp32 (the precision in which the GPU
+    decides the code); the rounding to E4M3FN is exact.
 
 All floating point here is float64 (numpy).  Indexer scores are returned as
 float32 after an exact float64 computation (integer-valued inputs keep every
@@ -289,3 +296,67 @@ def token_path(pool: PoolView, page_row, pos: int, q_idx, w, q, k: int,
                          sm_scale, tile, splits)
     o, lse = combine(o_p, lse_p)
     return dict(scores=scores, idx=idx, o=o, lse=lse)
+
+
+# ---------------------------------------------------------------------------
+# Writing new tokens into the cache (quantize + append)
+# ---------------------------------------------------------------------------
+_E4M3_POS = _E4M3[:0x7F]          # codes 0x00..0x7E: the finite non-negative values, ascending
+
+
+def e4m3fn_encode(y) -> np.ndarray:
+    """Nearest E4M3FN code of each float value: the finite code whose value is
+    closest to y (ties to the code with an even last bit), |y| saturated at 448,
+    the sign bit taken from y (so -0.0 and small negative values give 0x80)."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.minimum(np.abs(y), 448.0)
+    hi = np.searchsorted(_E4M3_POS, mag, side="left")          # first value >= mag
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_fp8_row(x) -> tuple[np.ndarray, np.ndarray]:
+    """One 576-element row (any float input; the GPU path takes bf16) -> (codes
+    uint8[576], scales float32[9]) with scale and x / scale formed in fp32."""
+    x32 = np.asarray(x, dtype=np.float32).reshape(FP8_NGROUPS, FP8_GROUP)
+    amax = np.abs(x32).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[:, None]).astype(np.float32)
+    return e4m3fn_encode(y).reshape(D_QK), scale
+
+
+def append_rows(pool: PoolView, page_table: np.ndarray, req, pos, latent, keys=None):
+    """Write rows into the pool bytes in place: row i goes to request req[i],
+    position pos[i] (page page_table[req[i]][pos[i] // 64], slot pos[i] % 64).
+    latent: [n, 576] floats (bf16 values for a BF16 pool); keys: [n, 128]
+    bf16 bit patterns or None.  Rows whose request, position or page id is out
+    of range are skipped."""
+    pt = np.asarray(page_table)
+    for i in range(len(req)):
+        b, p = int(req[i]), int(pos[i])
+        if not (0 <= b < pt.shape[0] and 0 <= p and p // PAGE_TOKENS < pt.shape[1]):
+            continue
+        page = int(pt[b, p // PAGE_TOKENS])
+        if not (0 <= page < pool.num_pages):
+            continue
+        phys = page * PAGE_TOKENS + p % PAGE_TOKENS
+        at = pool.lat_off + phys * pool.stride
+        if pool.kv_dtype == KV_FP8:
+            codes, scales = quantize_fp8_row(latent[i])
+            row = np.zeros(pool.stride, dtype=np.uint8)
+            row[:D_QK] = codes
+            row[FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 4 * FP8_NGROUPS] = scales.astype('<f4').view(np.uint8)
+        else:
+            row = np.asarray(latent[i], dtype=np.float32).view(np.uint32) >> np.uint32(16)
+            row = row.astype(np.uint16).view(np.uint8)
+            assert np.array_equal(bf16_bits_to_f64(row.view(np.uint16)),
+                                  np.asarray(latent[i], dtype=np.float64)), "BF16 pool takes bf16 values"
+        pool.buf[at:at + pool.stride] = row
+        if keys is not None:
+            ka = pool.idx_off + phys * KEY_ROW_BYTES
+            pool.buf[ka:ka + KEY_ROW_BYTES] = np.asarray(keys[i], dtype=np.uint16).view(np.uint8)

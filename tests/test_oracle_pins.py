@@ -370,3 +370,108 @@ def test_planted_mistakes_are_caught():
     unsorted = np.lexsort((np.arange(50), -scores))[:13]
     assert unsorted.tolist() != _brute_topk(scores.tolist(), 13)
     assert O.topk_positions(scores, 13).tolist() == _brute_topk(scores.tolist(), 13)
+
+
+# ---------------------------------------------------------------------------
+# Writing new tokens into the cache: E4M3FN encoder, row quantizer, append
+# ---------------------------------------------------------------------------
+def test_e4m3fn_encode_exact_values_ties_and_saturation():
+    codes = np.arange(0x7F)
+    vals = O.e4m3fn_table()[codes]
+    # every finite value encodes to its own code, both signs
+    assert np.array_equal(O.e4m3fn_encode(vals), codes.astype(np.uint8))
+    assert np.array_equal(O.e4m3fn_encode(-vals), (codes | 0x80).astype(np.uint8))
+    # exact midpoints go to the even code; a hair either side to the nearer one
+    mid = (vals[:-1] + vals[1:]) / 2
+    even = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:]).astype(np.uint8)
+    assert np.array_equal(O.e4m3fn_encode(mid), even)
+    eps = (vals[1:] - vals[:-1]) * 1e-3
+    assert np.array_equal(O.e4m3fn_encode(mid - eps), codes[:-1].astype(np.uint8))
+    assert np.array_equal(O.e4m3fn_encode(mid + eps), codes[1:].astype(np.uint8))
+    # closed-form points: 1.0 = 0x38, 448 = 0x7E, smallest subnormal 2^-9 = 0x01
+    assert list(O.e4m3fn_encode([1.0, 448.0, 2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -10])) == \
+        [0x38, 0x7E, 0x01, 0x00, 0x01]
+    # saturation (no infinity in E4M3FN, S.1111.111 is NaN): anything above 448
+    assert list(O.e4m3fn_encode([450.0, 464.0, 1e6, -1e6])) == [0x7E, 0x7E, 0x7E, 0xFE]
+    # the sign comes from the value: negative zero and tiny negatives give 0x80
+    assert list(O.e4m3fn_encode([-0.0, -1e-9, 0.0])) == [0x80, 0x80, 0x00]
+
+
+def test_e4m3fn_encode_matches_torch_cast():
+    # torch's float8_e4m3fn cast is round-to-nearest-even on in-range values
+    g = np.random.default_rng(11)
+    y = np.concatenate([g.standard_normal(100000) * 80, g.standard_normal(50000) * 0.01,
+                        g.uniform(-448, 448, 50000)]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3fn_encode(y), ref)
+
+
+def test_quantize_row_properties():
+    g = np.random.default_rng(12)
+    x = (g.standard_normal(576) * np.repeat(10.0 ** g.uniform(-3, 3, 9), 64)).astype(np.float32)
+    x[64:128] = 0.0                                  # an all-zero group
+    x[200] = -np.abs(x[128:192]).max() * 3           # a group dominated by one value
+    codes, scales = O.quantize_fp8_row(x)
+    xg = x.reshape(9, 64)
+    amax = np.abs(xg).max(axis=1)
+    assert scales[1] == np.float32(1.0) and np.all(codes[64:128] == 0)
+    want = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(scales, want)
+    # the largest magnitude of each non-zero group encodes to +-448
+    for gi in range(9):
+        if amax[gi] > 0:
+            j = 64 * gi + int(np.argmax(np.abs(xg[gi])))
+            assert codes[j] & 0x7F == 0x7E
+    # dequantized error: half an E4M3 step (<= 2^-4 relative for normals,
+    # 2^-10 * scale absolute in the subnormal range)
+    deq = O.e4m3fn_table()[codes] * np.repeat(scales.astype(np.float64), 64)
+    err = np.abs(deq - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, np.repeat(scales.astype(np.float64), 64) * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
+def test_quantize_row_matches_generator_quantizer():
+    # the seeded generator quantizes with torch ops; the same fp32 rows must
+    # give the same bytes through the oracle's quantizer
+    from sparse_attention_09_amd import synth
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn((40, 576), generator=g) * torch.rand((40, 1), generator=g) * 5
+    x[3, :64] = 0.0
+    rows = synth._quantize_fp8_rows(x).numpy()
+    for i in range(40):
+        codes, scales = O.quantize_fp8_row(x[i].numpy())
+        assert np.array_equal(rows[i, :576], codes)
+        assert np.array_equal(rows[i, 576:612].view('<f4'), scales)
+        assert np.all(rows[i, 612:] == 0)
+
+
+@pytest.mark.parametrize("kv_dtype", [O.KV_FP8, O.KV_BF16])
+def test_append_rows_round_trip_and_skips(kv_dtype):
+    num_pages = 6
+    total = O.pool_plane_offsets(kv_dtype, num_pages)[2]
+    pool = O.PoolView(np.zeros(total, dtype=np.uint8), num_pages, kv_dtype)
+    pt = np.array([[4, 1, 2], [5, 0, -1]], dtype=np.int32)
+    g = np.random.default_rng(14)
+    n = 5
+    lat = torch.from_numpy(g.standard_normal((n, 576)).astype(np.float32)).to(torch.bfloat16)
+    lat64 = lat.float().numpy().astype(np.float64)
+    keys = torch.from_numpy(g.integers(-8, 9, (n, 128)).astype(np.float32)).to(torch.bfloat16)
+    keys_bits = keys.view(torch.uint16).numpy()
+    req = [0, 0, 1, 1, 1]
+    pos = [0, 130, 65, 150, 999]          # (1, 150): page id -1; (1, 999): past the table
+    before = pool.buf.copy()
+    O.append_rows(pool, pt, req, pos, lat.float().numpy(), keys_bits)
+    for i in range(3):
+        row = pool.latent_rows(pt[req[i]], [pos[i]])[0]
+        if kv_dtype == O.KV_BF16:
+            assert np.array_equal(row, lat64[i])
+        else:
+            codes, scales = O.quantize_fp8_row(lat64[i])
+            assert np.array_equal(row, O.e4m3fn_table()[codes] * np.repeat(scales.astype(np.float64), 64))
+        assert np.array_equal(pool.index_keys(pt[req[i]], [pos[i]])[0], keys.float().numpy()[i])
+    # exactly three rows (and their keys) changed; the skipped ones wrote nothing
+    changed = np.nonzero(pool.buf != before)[0]
+    lat_rows = set((changed[changed < pool.idx_off] - pool.lat_off) // pool.stride)
+    key_rows = set((changed[changed >= pool.idx_off] - pool.idx_off) // O.KEY_ROW_BYTES)
+    want = {4 * 64 + 0, 2 * 64 + 2, 0 * 64 + 1}
+    assert lat_rows <= want and key_rows <= want and len(lat_rows) == 3
