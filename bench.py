@@ -54,6 +54,35 @@ def algorithmic_bytes(spec, plan, kv_row_bytes, fused=False):
     return d
 
 
+def time_kv_append(dsa, kv_dtype, dev, rows=32768, reps=20):
+    """Writing `rows` new tokens (latent + indexer key) into a scratch pool of
+    the workload's KV format: event time per call and algorithmic bytes."""
+    pages = (rows + 63) // 64
+    lay = dsa.pool_layout(kv_dtype, pages)
+    buf = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev)
+    pool = dsa.Pool(buf, pages, kv_dtype)
+    pt = torch.arange(pages, dtype=torch.int32, device=dev).view(1, pages)
+    req = torch.zeros(rows, dtype=torch.int32, device=dev)
+    pos = torch.arange(rows, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    lat = torch.randn((rows, 576), generator=g, device=dev).to(torch.bfloat16)
+    keys = torch.randint(-8, 9, (rows, 128), generator=g, device=dev).to(torch.bfloat16)
+    dsa.kv_append(pool, pt, req, pos, lat, keys)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dsa.kv_append(pool, pt, req, pos, lat, keys)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    out_row = (lay.latent_row_bytes if kv_dtype == dsa.KV_FP8 else 2 * 576) + 256
+    alg = rows * (576 * 2 + 128 * 2 + 8 + out_row)
+    pool.close()
+    return {"rows": rows, "avg_us": round(us, 3), "alg_bytes": alg,
+            "gbps": round(alg / (us * 1e-6) / 1e9, 1)}
+
+
 def flops(spec):
     T, k = spec.num_tokens, spec.k
     vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
@@ -314,6 +343,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    result["kv_append"] = time_kv_append(dsa, spec.kv_dtype, dev)
     if args.calibrate_copy:
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)

@@ -235,6 +235,26 @@ dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_table, int32
 dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,
                        int32_t num_splits, uint16_t* out, float* lse, void* stream);
 
+/* Writing new tokens into the cache [SGL "Size both memory pools": the paged
+ * KV pool, FP8 by default on MI355X, and the separate DSA indexer pool].  Row i of the batch goes to
+ * request req[i], position pos[i]: page page_table[req[i]*pt_stride +
+ * pos[i]/64], slot pos[i] % 64, in both planes.
+ *   latent: bf16 [n,576] (512 latent + 64 rope), 16-byte aligned;
+ *   keys:   bf16 [n,128] indexer keys, 16-byte aligned, or NULL to leave the
+ *           indexer plane untouched.
+ * FP8 pools (reading of the quantizer, not spelled out by the pages): per 64
+ * consecutive elements scale = amax/448 in fp32 (1 for an all-zero group),
+ * code = E4M3FN(x/scale) rounded to the nearest finite value, ties to the
+ * even code, saturated at 448 (x/scale formed in fp32); the nine scales
+ * follow the codes and the 28 pad bytes are written as 0.  BF16 pools: the
+ * 576 values are copied.  Rows whose request (outside [0,num_reqs)),
+ * position (negative or past the page table) or page id (outside the pool)
+ * is out of range are skipped.  Two rows with one destination: unspecified
+ * which lands.  Asynchronous on `stream` like every compute call. */
+dsa_status dsa_kv_append(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                         int32_t num_reqs, const int32_t* req, const int32_t* pos, int32_t n,
+                         const uint16_t* latent, const uint16_t* keys, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

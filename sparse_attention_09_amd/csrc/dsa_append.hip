@@ -1,0 +1,131 @@
+// Writing new tokens into the cache on gfx950: quantize + append.
+//
+// "GLM-5.3-Flash" SGLang cookbook, section 2 ("Size both memory pools"): the
+// paged KV pool holds the latent rows - FP8 by default on MI355X - and the DSA
+// indexer pool the indexer keys.  The pages do not spell the quantizer out;
+// the reading used here (and by the oracle): per group of 64 consecutive
+// elements, scale = amax / 448 in fp32 (1 for an all-zero group) and
+// code = E4M3FN(x / scale), rounded to the nearest finite value with ties to
+// the even code and saturated at 448; the row's 28 pad bytes are written as 0.
+//
+// One wave per row.  Lane l holds elements 64g + l of the nine groups, so a
+// group's amax is one wave reduction and its 64 codes one coalesced 64-byte
+// store.  The E4M3 rounding is done with integer operations on the fp32 bits
+// (exact, independent of any hardware conversion mode).
+#include <hip/hip_runtime.h>
+
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace {
+
+using dsa::u32x4;
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+constexpr int kGroups = DSA_D_QK / 64;         // 9
+constexpr int kFp8Stride = 640;
+constexpr int kBf16Stride = 2 * DSA_D_QK;
+
+// Nearest E4M3FN code of a finite fp32 value (ties to even, |y| saturated at
+// 448, sign from y).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below 2^-6 the grid is the subnormals, step 2^-9: a*512 is exact and
+    // rint rounds half to even (8 is the smallest normal, code 0x08)
+    code = uint32_t(__builtin_rintf(a * 512.f));
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t e = (bits >> 23) - 127u + 7u;   // biased E4M3 exponent, 1..15
+    const uint32_t m = bits & 0x7FFFFFu;
+    const uint32_t m3 = m >> 20, rem = m & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
+    code = min((e << 3) + m3 + up, 0x7Eu);       // a mantissa carry moves up the exponent
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return dsa::rows4_max(v);
+}
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    uint8_t* __restrict__ latent, uint8_t* __restrict__ key_plane, int num_pages,
+    const int32_t* __restrict__ page_table, int pt_stride, int num_reqs,
+    const int32_t* __restrict__ req, const int32_t* __restrict__ pos, int n,
+    const uint16_t* __restrict__ src, const uint16_t* __restrict__ ksrc) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int b = req[i], p = pos[i];
+  if (b < 0 || b >= num_reqs || p < 0 || (p >> 6) >= pt_stride) return;
+  const int page = page_table[int64_t(b) * pt_stride + (p >> 6)];
+  if (page < 0 || page >= num_pages) return;
+  const int64_t phys = int64_t(page) * DSA_PAGE_TOKENS + (p & (DSA_PAGE_TOKENS - 1));
+  const uint16_t* x = src + int64_t(i) * DSA_D_QK;
+
+  if constexpr (KV == DSA_KV_FP8_E4M3_S64) {
+    uint8_t* row = latent + phys * kFp8Stride;
+    float v[kGroups], scale[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) v[g] = dsa::bf16_bits_to_f32(x[64 * g + lane]);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const float amax = wave_max(fabsf(v[g]));
+      scale[g] = amax > 0.f ? amax / 448.f : 1.f;
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) row[64 * g + lane] = uint8_t(e4m3_encode(v[g] / scale[g]));
+    // scales at byte 576 (lanes 0..8), zero padding up to byte 640 (lanes 9..15)
+    float sv = 0.f;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) sv = lane == g ? scale[g] : sv;
+    if (lane < 16) reinterpret_cast<float*>(row + DSA_D_QK)[lane] = sv;
+  } else {
+    u32x4* row = reinterpret_cast<u32x4*>(latent + phys * kBf16Stride);
+    const u32x4* s16 = reinterpret_cast<const u32x4*>(x);
+    row[lane] = s16[lane];
+    if (lane < kBf16Stride / 16 - 64) row[64 + lane] = s16[64 + lane];
+  }
+  if (ksrc && lane < 16) {
+    reinterpret_cast<u32x4*>(key_plane + phys * (2 * DSA_IDX_DIM))[lane] =
+        reinterpret_cast<const u32x4*>(ksrc + int64_t(i) * DSA_IDX_DIM)[lane];
+  }
+}
+
+}  // namespace
+
+extern "C" dsa_status dsa_kv_append(const dsa_pool* pool, const int32_t* page_table,
+                                    int32_t pt_stride, int32_t num_reqs, const int32_t* req,
+                                    const int32_t* pos, int32_t n, const uint16_t* latent,
+                                    const uint16_t* keys, void* stream) {
+  if (!pool) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: pool is null");
+  if (n < 0 || num_reqs < 0 || pt_stride < 1)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: need n >= 0, num_reqs >= 0, pt_stride >= 1");
+  if (n == 0) return dsa::ok();
+  if (!page_table || !req || !pos || !latent)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: page_table, req, pos and latent must be non-null");
+  if (!dsa::aligned(latent, 16) || (keys && !dsa::aligned(keys, 16)) || !dsa::aligned(req, 4) ||
+      !dsa::aligned(pos, 4) || !dsa::aligned(page_table, 4))
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: latent and keys must be 16-byte aligned");
+  uint8_t* lat = reinterpret_cast<uint8_t*>(pool->base + pool->layout.latent_plane_offset);
+  uint8_t* kp = reinterpret_cast<uint8_t*>(pool->base + pool->layout.index_plane_offset);
+  const dim3 grid{unsigned((n + kRowsPerBlock - 1) / kRowsPerBlock)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pool->kv_dtype == DSA_KV_FP8_E4M3_S64)
+    hipLaunchKernelGGL(append_kernel<DSA_KV_FP8_E4M3_S64>, grid, dim3(kThreads), 0, st, lat, kp,
+                       pool->num_pages, page_table, pt_stride, num_reqs, req, pos, n, latent, keys);
+  else
+    hipLaunchKernelGGL(append_kernel<DSA_KV_BF16>, grid, dim3(kThreads), 0, st, lat, kp,
+                       pool->num_pages, page_table, pt_stride, num_reqs, req, pos, n, latent, keys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string("dsa_kv_append: launch failed: ") + hipGetErrorString(e));
+  return dsa::ok();
+}

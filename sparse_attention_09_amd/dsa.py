@@ -38,7 +38,7 @@ EXPORTS = [
     "dsa_pool_share", "dsa_pool_release", "dsa_pool_free_pages", "dsa_pool_refcount",
     "dsa_pool_num_pages", "dsa_pool_kv_dtype",
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
-    "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine",
+    "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
 ]
 
 
@@ -104,6 +104,7 @@ def lib() -> ctypes.CDLL:
             "dsa_sparse_mla": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32, vp, vp,
                                      vp]),
             "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+            "dsa_kv_append": (i32, [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -320,6 +321,22 @@ def combine(o_part: torch.Tensor, lse_part: torch.Tensor, out=None, lse=None):
     _check(lib().dsa_combine(_ptr(o_part), _ptr(lse_part), T, S, _ptr(out), _ptr(lse),
                              _stream(dev)))
     return out, lse
+
+
+def kv_append(pool: Pool, page_table, req, pos, latent, keys=None):
+    """Quantize (FP8 pools) or copy (BF16 pools) new latent rows, with their
+    indexer keys, into the pool at (request, position)."""
+    dev = pool.device
+    n = req.numel()
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(req, "req", torch.int32, dev, (n,))
+    _need(pos, "pos", torch.int32, dev, (n,))
+    _need(latent, "latent", torch.bfloat16, dev, (n, D_QK))
+    if keys is not None:
+        _need(keys, "keys", torch.bfloat16, dev, (n, IDX_DIM))
+    _check(lib().dsa_kv_append(pool.handle, _ptr(page_table), page_table.shape[-1],
+                               page_table.shape[0], _ptr(req), _ptr(pos), n, _ptr(latent),
+                               _ptr(keys), _stream(dev)))
 
 
 def default_sm_scale() -> float:

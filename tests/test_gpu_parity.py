@@ -160,6 +160,44 @@ def test_single_split_call_equals_partial_plus_combine(name):
         assert torch.equal(lse_a, lse_b)
 
 
+@pytest.mark.parametrize("name", ["tiny_fp8", "tiny_bf16"])
+def test_kv_append_matches_oracle_bytes(name):
+    # new tokens written into the pool by the GPU and by the oracle's
+    # quantizer/append on a host copy: every byte of the pool must agree
+    # (FP8 codes and scales bit-exact; rows with an out-of-range request,
+    # position or page id write nothing)
+    wl = synth.generate(synth.spec(name), seed=8, device="cpu")
+    g = torch.Generator().manual_seed(88)
+    B = wl.page_table.shape[0]
+    n_pos = wl.page_table.shape[1] * 64
+    # distinct destinations inside the requests' contexts (unused page-table
+    # entries alias page 0, and two rows with one destination are unspecified)
+    cand = torch.tensor([(b, p) for b, L in enumerate(wl.spec.ctx_lens) for p in range(L)])
+    pick = cand[torch.randperm(cand.shape[0], generator=g)[:300]]
+    req = pick[:, 0].to(torch.int32).contiguous()
+    pos = pick[:, 1].to(torch.int32).contiguous()
+    req[:3] = torch.tensor([B, -1, 0], dtype=torch.int32)            # bad request ids
+    pos[2] = n_pos                                                     # past the page table
+    n = req.numel()
+    scale = torch.exp(torch.randn((n, 9), generator=g) * 4).repeat_interleave(64, dim=1)
+    lat = (torch.randn((n, 576), generator=g) * scale).to(torch.bfloat16)
+    lat[5, 64:128] = 0.0                                               # an all-zero group
+    lat[6, :64] = -0.0                                                 # negative zeros
+    lat[7, 128:192] = torch.randn(64, generator=g).to(torch.bfloat16) * 1e-30
+    keys = torch.randint(-8, 9, (n, 128), generator=g).to(torch.bfloat16)
+    pool_host = O.PoolView(wl.pool.numpy().copy(), wl.num_pages, wl.spec.kv_dtype)
+    O.append_rows(pool_host, wl.page_table.numpy(), req.tolist(), pos.tolist(),
+                  lat.float().numpy(), keys.view(torch.uint16).numpy())
+    dev = wl.to(DEV)
+    pool = make_pool(dev)
+    say(f"[case] kv_append {name}: {n} rows")
+    dsa.kv_append(pool, dev.page_table, req.to(DEV), pos.to(DEV), lat.to(DEV), keys.to(DEV))
+    torch.cuda.synchronize()
+    got = dev.pool.cpu().numpy()
+    bad = np.nonzero(got != pool_host.buf)[0]
+    assert bad.size == 0, f"{bad.size} pool bytes differ, first at {bad[:8]}"
+
+
 def test_all_masked_token_gives_zero_and_neg_inf():
     wl = _gen("tiny_fp8", seed=4)
     pool = make_pool(wl)

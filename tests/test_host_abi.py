@@ -228,6 +228,15 @@ def test_compute_calls_validate_before_launch():
     # combine
     assert L.dsa_combine(f, f, 1, 0, f, f, None) == 1
     assert L.dsa_combine(None, f, 1, 1, f, f, None) == 1
+    # cache append: pool, sizes, pointers, alignment
+    assert L.dsa_kv_append(None, f, 4, 1, f, f, 1, f, f, None) == 1
+    assert L.dsa_kv_append(h, f, 4, 1, f, f, -1, f, f, None) == 1
+    assert L.dsa_kv_append(h, f, 0, 1, f, f, 1, f, f, None) == 1
+    assert L.dsa_kv_append(h, f, 4, 1, None, f, 1, f, f, None) == 1
+    assert L.dsa_kv_append(h, f, 4, 1, f, f, 1, None, f, None) == 1
+    assert L.dsa_kv_append(h, f, 4, 1, f, f, 1, vp(FAKE + 8), None, None) == 1
+    assert L.dsa_kv_append(h, f, 4, 1, f, f, 1, f, vp(FAKE + 4), None) == 1
+    assert L.dsa_kv_append(h, None, 4, 1, None, None, 0, None, None, None) == 0
     # empty batches are valid no-ops
     assert L.dsa_combine(None, None, 0, 1, None, None, None) == 0
     assert L.dsa_topk(None, 64, None, 0, 64, 8, None, None, 0, None) == 0
