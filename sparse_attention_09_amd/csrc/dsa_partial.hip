@@ -513,7 +513,8 @@ constexpr float kOverflowSum = 4503599627370496.f;   // 2^52
 template <int TILE>
 struct SmemV2 {
   static constexpr int kPStride = TILE + 8;     // bf16 per head in the P buffer
-  uint16_t k[TILE * kKStride];
+  static constexpr int kNBuf = TILE == 32 ? 2 : 1;   // K tiles (double buffer at 32 rows)
+  uint16_t k[kNBuf][TILE * kKStride];
   int32_t rows[kRowChunk];
   float bias[kRowChunk];                        // 0 for a valid row, -inf for a masked one
   f32x4 xs[8][TILE / 32][64];                   // partial S^T sent to the dh partner
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   // P: written at head 32hp + 16dh + c, read as the A operand of head 32hp + 16hb + c
   uint16_t* pw = sm.p + (32 * hp + 16 * dh + c) * kPS;
 
-  auto compute_tile = [&](int it, const uint16_t* kt) {
+  auto compute_tile = [&](int it, const uint16_t* kt, auto&& after_qk) {
     // S^T over this wave's rows and half of the dims, starting at the row bias
     f32x4 sacc[kOMB][2];
 #pragma unroll
@@ -591,6 +592,9 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
           sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
                                            sacc[mb][hb]);
     }
+    // work that needs no result of this tile (the next tile's staging with a
+    // double buffer) sits here, next to the MFMAs, for the scheduler to interleave
+    after_qk();
     // keep head block dh, send head block 1-dh to the partner (wave ^ 2)
     f32x4 sv[kOMB];
 #pragma unroll
@@ -687,16 +691,32 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       __syncthreads();
       const int ntile = (cend - cc + TILE - 1) / TILE;
       st.load(a.latent, sm.rows, tid);
-      st.store(sm.k, 0, tid);
-      __syncthreads();
-      for (int it = 0; it < ntile; ++it) {
-        const bool more = it + 1 < ntile;
-        if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
-        compute_tile(it, sm.k);
+      st.store(sm.k[0], 0, tid);
+      if constexpr (SmemV2<TILE>::kNBuf == 2) {
+        // tile it+1 waits in registers; during tile it it goes to the other
+        // buffer (free since the last barrier) and tile it+2 is fetched.  Both
+        // run unconditionally (row indices clamped into the chunk): past the
+        // last tile they refill the idle buffer with data nobody reads.
+        st.load(a.latent, sm.rows + min(1, ntile - 1) * TILE, tid);
         __syncthreads();
-        if (more) {
-          st.store(sm.k, 0, tid);
+        for (int it = 0; it < ntile; ++it) {
+          compute_tile(it, sm.k[it & 1], [&] {
+            st.store(sm.k[(it + 1) & 1], 0, tid);
+            st.load(a.latent, sm.rows + min(it + 2, ntile - 1) * TILE, tid);
+          });
           __syncthreads();
+        }
+      } else {
+        __syncthreads();
+        for (int it = 0; it < ntile; ++it) {
+          const bool more = it + 1 < ntile;
+          if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
+          compute_tile(it, sm.k[0], [] {});
+          __syncthreads();
+          if (more) {
+            st.store(sm.k[0], 0, tid);
+            __syncthreads();
+          }
         }
       }
     }
