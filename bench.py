@@ -1,7 +1,8 @@
 """Benchmark of the DSA sparse-attention path on one MI355X.
 
-One step = the whole path over one batch: indexer scores -> top-k -> sparse
-MLA partial -> combine, with inputs resident in HBM.  Default workload: the
+One step = the whole path over one batch: indexer scores -> top-k (fused into
+one call without a score matrix for rows up to 65,536) -> sparse MLA partial
+-> combine, with inputs resident in HBM.  Default workload: the
 speculative-verify decode batch, 128 requests x 8 query tokens, 64K context
 each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
 64 heads.  Prints ONE JSON line.
@@ -28,7 +29,9 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
 
 def algorithmic_bytes(spec, plan, kv_row_bytes, fused=False):
     """Bytes each kernel must move at minimum, per launch (one step).  With one
-    split (fused) Partial writes the bf16 output and lse itself; no Combine."""
+    split (fused) Partial writes the bf16 output and lse itself; no Combine.
+    The fused selection (index_topk) must read the keys and queries and write
+    the indices; its samples and candidates are overhead, not counted."""
     T = spec.num_tokens
     k = spec.k
     S = plan.splits
@@ -44,6 +47,8 @@ def algorithmic_bytes(spec, plan, kv_row_bytes, fused=False):
         "index_scores": keys + T * (16 * 128 * 2 + 16 * 4) + vis * 4,
         # visible score reads + index writes
         "topk": vis * 4 + T * k * 4,
+        # keys + indexer queries/weights + index writes
+        "index_topk": keys + T * (16 * 128 * 2 + 16 * 4) + T * k * 4,
     }
     attend_in = T * k * 4 + T * k * kv_row_bytes + T * 64 * 576 * 2   # index, selected rows, q
     if fused:
@@ -87,7 +92,8 @@ def flops(spec):
     T, k = spec.num_tokens, spec.k
     vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
               for p in range(L - q, L))
-    return {"index_scores": vis * 16 * 128 * 2, "partial": T * 64 * k * (576 + 512) * 2}
+    return {"index_scores": vis * 16 * 128 * 2, "index_topk": vis * 16 * 128 * 2,
+            "partial": T * 64 * k * (576 + 512) * 2}
 
 
 def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
@@ -131,10 +137,20 @@ def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 
-KERNEL_PATTERNS = {"index_scores": "index_scores", "topk": "topk_kernel", "partial": "partial",
-                   "combine": "combine_kernel"}
-KERNEL_SOURCES = {"index_scores": "dsa_index.hip", "topk": "dsa_topk.hip",
-                  "partial": "dsa_partial.hip", "combine": "dsa_partial.hip"}
+# rocprofv3 kernel names (mangled or demangled) -> path step.  The fused
+# selection (index_topk) is five launches: sample pass, threshold, emit pass,
+# select, fallback.
+KERNEL_PATTERNS = [
+    ("index_scores", r"index_kernel(ILi0E|<0>)"), ("index_sample", r"index_kernel(ILi1E|<1>)"),
+    ("index_emit", r"index_kernel(ILi2E|<2>)"), ("threshold", r"threshold_kernel"),
+    ("select", r"select_kernel"), ("fallback", r"fallback_kernel"), ("topk", r"topk_kernel"),
+    ("partial", r"partial"), ("combine", r"combine_kernel")]
+FUSED_SELECT = ("index_sample", "threshold", "index_emit", "select", "fallback")
+KERNEL_SOURCES = {"index_scores": ("dsa_index.hip",), "topk": ("dsa_topk.hip",),
+                  "index_topk": ("dsa_index.hip", "dsa_topk.hip"),
+                  "partial": ("dsa_partial.hip",), "combine": ("dsa_partial.hip",)}
+for _k in FUSED_SELECT:
+    KERNEL_SOURCES[_k] = KERNEL_SOURCES["index_topk"]
 CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
 
 
@@ -142,15 +158,16 @@ def source_sha(kernel: str) -> str:
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "dsa_device.h"):
+    for f in KERNEL_SOURCES[kernel] + ("dsa_device.h",):
         with open(os.path.join(root, "sparse_attention_09_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def _kernel_of(name: str):
-    for k, pat in KERNEL_PATTERNS.items():
-        if pat in name:
+    import re
+    for k, pat in KERNEL_PATTERNS:
+        if re.search(pat, name):
             return k
     return None
 
@@ -161,12 +178,20 @@ def summarize_stats(csv_path: str, command: str) -> str:
     rows = list(csv.DictReader(open(csv_path)))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "#",
              f"{'kernel':14s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}  name"]
+    fused = {}
     for r in rows:
         k = _kernel_of(r["Name"])
         if k is None:
             continue
         lines.append(f"{k:14s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}  {r['Name'][:90]}")
+        if k in FUSED_SELECT:
+            fused[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    if fused:
+        # one fused selection call = one launch of each of its kernels
+        calls = max(c for c, _ in fused.values())
+        lines.append(f"{'index_topk':14s} {calls:6d} {sum(a for _, a in fused.values()):10.2f} "
+                     f"{'':>10s} {'':>10s}  sum of the averages of: {', '.join(sorted(fused))}")
     return "\n".join(lines) + "\n"
 
 
@@ -206,6 +231,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands: list)
         out["kernels"][k] = {"fetch_kib": fetch.get(k), "write_kib": write.get(k),
                              "read_bytes": int(fb), "write_bytes": int(wb),
                              "traffic_bytes": int(fb + wb), "source_sha": source_sha(k)}
+    parts = [k for k in FUSED_SELECT if k in out["kernels"]]
+    if parts:
+        # one fused selection call = one launch of each of its kernels
+        rb = sum(out["kernels"][k]["read_bytes"] for k in parts)
+        wb = sum(out["kernels"][k]["write_bytes"] for k in parts)
+        out["kernels"]["index_topk"] = {"parts": parts, "read_bytes": rb, "write_bytes": wb,
+                                        "traffic_bytes": rb + wb,
+                                        "source_sha": source_sha("index_topk")}
     return out
 
 
@@ -239,6 +272,9 @@ def main():
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--select", default="auto", choices=["auto", "fused", "scores"],
+                    help="top-k selection: fused indexer + top-k (auto: rows up to 65,536) "
+                         "or the score matrix + top-k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
@@ -262,9 +298,10 @@ def main():
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx, spec.k,
                        kv_tile=args.tile, num_splits=args.splits, sm_scale=spec.sm_scale,
-                       cu_count=cus)
+                       cu_count=cus, select=args.select)
     plan = path.plan
-    print(f"[bench] plan tile={plan.tile} splits={plan.splits} cus={cus}", file=sys.stderr, flush=True)
+    print(f"[bench] plan tile={plan.tile} splits={plan.splits} cus={cus} "
+          f"selection={'fused' if path.fused_topk else 'scores+topk'}", file=sys.stderr, flush=True)
 
     def step():
         path.step(wl.q_idx, wl.w, wl.q)
@@ -287,13 +324,18 @@ def main():
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     # per-kernel timing on the same stream (separate loop, events between calls)
-    if path.fused:
-        names = ["index_scores", "topk", "partial"]
-        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk, lambda: path.attend(wl.q)]
+    if path.fused_topk:
+        names = ["index_topk"]
+        calls = [lambda: path.index_topk(wl.q_idx, wl.w)]
     else:
-        names = ["index_scores", "topk", "partial", "combine"]
-        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk,
-                 lambda: path.partial(wl.q), path.combine]
+        names = ["index_scores", "topk"]
+        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk]
+    if path.fused:
+        names += ["partial"]
+        calls += [lambda: path.attend(wl.q)]
+    else:
+        names += ["partial", "combine"]
+        calls += [lambda: path.partial(wl.q), path.combine]
     acc = {n: 0.0 for n in names}
     for _ in range(args.steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -305,6 +347,27 @@ def main():
         for i, n in enumerate(names):
             acc[n] += evs[i].elapsed_time(evs[i + 1])
     per_us = {n: 1000.0 * acc[n] / args.steps for n in names}
+    fallback_tokens = path.fallback_count()
+    unfused = None
+    if path.fused_topk:
+        # the same selection through the score matrix, for comparison (not in the step)
+        path.index_scores(wl.q_idx, wl.w)
+        path.topk()
+        torch.cuda.synchronize()
+        u = {"index_scores": 0.0, "topk": 0.0}
+        for _ in range(args.steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            evs[0].record(stream)
+            path.index_scores(wl.q_idx, wl.w)
+            evs[1].record(stream)
+            path.topk()
+            evs[2].record(stream)
+            torch.cuda.synchronize()
+            u["index_scores"] += evs[0].elapsed_time(evs[1])
+            u["topk"] += evs[1].elapsed_time(evs[2])
+        unfused = {n: round(1000.0 * v / args.steps, 3) for n, v in u.items()}
+        path.scores = path.workspace = None
+        torch.cuda.empty_cache()
 
     lay = dsa.pool_layout(spec.kv_dtype, 1)
     byts = algorithmic_bytes(spec, plan, lay.latent_row_bytes, path.fused)
@@ -337,12 +400,17 @@ def main():
                    "context": int(max(spec.ctx_lens)), "top_k": spec.k, "heads": 64,
                    "kv": "fp8_e4m3_s64" if spec.kv_dtype == dsa.KV_FP8 else "bf16",
                    "kv_tile": plan.tile, "splits": plan.splits,
-                   "combine": "in partial (one split)" if path.fused else "separate kernel"},
+                   "combine": "in partial (one split)" if path.fused else "separate kernel",
+                   "selection": "fused indexer + top-k" if path.fused_topk
+                   else "score matrix + top-k"},
         "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
                 "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
         "kernels": kernels,
         "roofline": roof,
     }
+    if path.fused_topk:
+        result["fused_select"] = {"fallback_tokens": fallback_tokens, "cap": path.cap,
+                                  "unfused_us": unfused}
     result["kv_append"] = time_kv_append(dsa, spec.kv_dtype, dev)
     if args.calibrate_copy:
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)

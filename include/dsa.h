@@ -175,6 +175,33 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos, int
                     int32_t max_ctx, int32_t k, int32_t* idx, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Fused indexer + top-k [LMSYS-1 indexer and selection; the blog's "top-k
+ * v2" change; the fused selection is this library's design]: the same idx as
+ * dsa_index_scores followed by dsa_topk (bit for bit), without a score
+ * matrix.  Arguments are those two calls' (scores/ld dropped), plus:
+ *   cap: candidate slots per token and 512-position chunk, 1..128 (128 is
+ *     ample for k = 2048 rows of 16K+ positions; denser rows overflow and
+ *     take the fallback);
+ *   cand_target: how many candidates per row the sampled threshold aims at,
+ *     or 0 = 2k.
+ * How: an indexer pass over one page in 32 gives per-token sample scores;
+ * their rank statistic sets a threshold; a full indexer pass keeps only the
+ * positions that reach it; an exact selection over those candidates gives the
+ * top-k whenever no chunk overflowed `cap` and at least k candidates exist.
+ * Other tokens are recomputed exactly by a one-workgroup-per-token fallback.
+ * max_ctx <= 65536 (DSA_ERR_UNSUPPORTED above).  workspace: device, 256-byte
+ * aligned, at least dsa_index_topk_workspace_bytes(num_tokens, max_ctx, cap)
+ * bytes, caller-owned; after the call completes its first int32 holds the
+ * number of tokens that took the fallback.  Calls sharing a workspace must
+ * be ordered on one stream. */
+size_t dsa_index_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t cap);
+dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                          const int32_t* q_offsets, int32_t num_reqs, int32_t max_q,
+                          const int32_t* tok_pos, int32_t num_tokens, int32_t max_ctx,
+                          const uint16_t* q_idx, const float* w, int32_t k, int32_t cap,
+                          int32_t cand_target, int32_t* idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Dispatch plan of the Partial step [LMSYS-3 and Figure 4].  Host-only.
  *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose.
  *   num_splits: KV splits per token, or 0 = choose from query parallelism

@@ -69,6 +69,38 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Indexer epilogue of one 16-position MFMA block (acc holds heads 4g..4g+3 of
+// position lane%16, g = lane/16): relu, head weights and the sum over all 16
+// heads.  Every lane receives the score of position lane%16; the order of the
+// additions is fixed, so every kernel using this gets the same bits.  relu is
+// a signed-integer max with 0 on the float bits (one op; -0 and negative
+// values give +0; NaN inputs are unsupported).
+__device__ __forceinline__ float index_score(const f32x4& acc, const float (&w)[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s = fmaf(w[j], __int_as_float(max(__float_as_int(acc[j]), 0)), s);
+  return rows4_sum(s);
+}
+
+// The same for two tokens' blocks at once: lanes 0..31 receive token A's score
+// of position lane%16, lanes 32..63 token B's.  One permlane32 swap pairs A's
+// groups 0+2 / 1+3 in the low half and B's in the high half, one permlane16
+// swap adds the pairs: the additions are those of index_score, in the same
+// order, so each token's bits equal index_score's.
+__device__ __forceinline__ float index_score2(const f32x4& accA, const float (&wA)[4],
+                                              const f32x4& accB, const float (&wB)[4]) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a = fmaf(wA[j], __int_as_float(max(__float_as_int(accA[j]), 0)), a);
+    b = fmaf(wB[j], __int_as_float(max(__float_as_int(accB[j]), 0)), b);
+  }
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
   const uint32_t u = __float_as_uint(f);

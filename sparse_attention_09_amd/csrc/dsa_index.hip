@@ -15,6 +15,8 @@
 // weights and the 16-head sum happen in registers and cross-lane shuffles.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -22,46 +24,69 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kQB = 8;             // query tokens per workgroup
-#ifndef DSA_INDEX_CHUNK_PAGES
-#define DSA_INDEX_CHUNK_PAGES 8
-#endif
-constexpr int kChunkPages = DSA_INDEX_CHUNK_PAGES;   // pages per workgroup
-constexpr int kKeyStride = 136;    // LDS stride of one key row in bf16 (128 + 8 pad)
+constexpr int kChunkPages = dsa::kIndexChunkPages;   // pages per workgroup
+// LDS page: 64 key rows of 256 bytes, unpadded; 16-byte chunk j of row r sits
+// at chunk j ^ (r & 15), so the 16 rows an MFMA operand read touches, and the
+// 16 chunks a staging write touches, fall in 16 different bank groups
+constexpr int kRowBf16 = DSA_IDX_DIM;
+constexpr int kCandLds = dsa::kIndexMaxCap;   // emit pass: candidate slots per token (LDS)
 constexpr int kPageKeysBf16 = DSA_PAGE_TOKENS * DSA_IDX_DIM;
+constexpr int kSampleStride = dsa::kIndexSampleStride;
+constexpr int kSampleChunkPages = 2;   // sample pass: sampled pages per workgroup
+
+enum Mode { kScores = 0, kSample = 1, kEmit = 2 };
 
 using dsa::bf16x8;
 using dsa::f32x4;
 using dsa::u32x4;
 
-__global__ __launch_bounds__(kThreads) void index_scores_kernel(
+// One work unit: request `req`, query block `qblock` (up to 8 tokens), chunk
+// `chunk` of pages.  Contains barriers; every thread of the workgroup runs it
+// with the same unit.  lds: two staging buffers of one page; cand_v/cand_p:
+// the emit pass's per-token candidate rows.
+template <int MODE>
+__device__ __forceinline__ void index_unit(
     const uint16_t* __restrict__ keys, int num_pages, const int32_t* __restrict__ page_table,
     int pt_stride, const int32_t* __restrict__ q_offsets, const int32_t* __restrict__ tok_pos,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, float* __restrict__ scores,
-    int64_t ld, int max_ctx, int num_tokens) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][DSA_PAGE_TOKENS * kKeyStride];
+    int64_t ld, int max_ctx, int num_tokens, const dsa::IndexEmit& em,
+    uint16_t (&lds)[2][DSA_PAGE_TOKENS * kRowBf16], float* cand_v, uint16_t* cand_p, int chunk,
+    int req, int qblock) {
+  // the sample pass visits logical pages 0, 32, 64, ... (its "page" pg is the
+  // sample page, logical page 32 pg); the other modes visit every page
+  constexpr int kStride = MODE == kSample ? kSampleStride : 1;
+  constexpr int kPages = MODE == kSample ? kSampleChunkPages : kChunkPages;
 
-  const int b = blockIdx.y;
-  const int t_begin = q_offsets[b] + blockIdx.z * kQB;
+  const int b = req;
+  const int t_begin = q_offsets[b] + qblock * kQB;
   const int t_end = min(min(q_offsets[b + 1], t_begin + kQB), num_tokens);
   const int nq = t_end - t_begin;
   if (nq <= 0) return;
   int block_max = -1;
   for (int t = t_begin; t < t_end; ++t) block_max = max(block_max, min(tok_pos[t], max_ctx - 1));
-  const int p_begin = blockIdx.x * kChunkPages * DSA_PAGE_TOKENS;
+  const int p_begin = chunk * kPages * kStride * DSA_PAGE_TOKENS;
   if (p_begin > block_max) return;
-  const int page_begin = blockIdx.x * kChunkPages;
-  const int page_end = min(min(page_begin + kChunkPages, block_max / DSA_PAGE_TOKENS + 1), pt_stride);
-  if (page_end <= page_begin) return;
-
+  const int page_begin = chunk * kPages;
+  const int last_lp = min(block_max / DSA_PAGE_TOKENS, pt_stride - 1);
+  const int page_end = min(page_begin + kPages, last_lp / kStride + 1);
   const int tid = threadIdx.x;
+  if (page_end <= page_begin) {
+    // only when the page table is shorter than the context: no candidates
+    if constexpr (MODE == kEmit)
+      for (int i = tid; i < nq; i += kThreads) em.count[int64_t(t_begin + i) * em.nch + chunk] = 0;
+    return;
+  }
+
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;   // lane group: MFMA k-slice / output row group
   const int c = lane & 15;   // MFMA row (A) / column (B, D)
 
-  // Wave -> (token pair, subset of the page's four 16-position blocks).
+  // Wave -> (token pair, subset of the page's four 16-position blocks).  The
+  // emit pass keeps each token's positions in one wave, so its candidates come
+  // out in position order.
   const int npair = (nq + 1) >> 1;
-  const int pairs_p2 = npair <= 1 ? 1 : (npair <= 2 ? 2 : 4);
+  const int pairs_p2 = MODE == kEmit ? 4 : (npair <= 1 ? 1 : (npair <= 2 ? 2 : 4));
   const int nsub = 4 / pairs_p2;
   const int pair = wave % pairs_p2;
   const int sub = wave / pairs_p2;
@@ -76,6 +101,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   u32x4 qa[4], qb[4];
   float wa[4], wb[4];
   int posA = -1, posB = -1;
+  float thrA = 0.f, thrB = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     qa[ks] = u32x4{0, 0, 0, 0};
@@ -90,6 +116,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) wa[j] = w[int64_t(tA) * DSA_IDX_HEADS + 4 * g + j];
     posA = min(tok_pos[tA], max_ctx - 1);
+    if constexpr (MODE == kEmit) thrA = em.thr[tA];
   }
   if (hasB) {
     const u32x4* src = reinterpret_cast<const u32x4*>(q_idx + (int64_t(tB) * DSA_IDX_HEADS + c) * DSA_IDX_DIM);
@@ -98,16 +125,31 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) wb[j] = w[int64_t(tB) * DSA_IDX_HEADS + 4 * g + j];
     posB = min(tok_pos[tB], max_ctx - 1);
+    if constexpr (MODE == kEmit) thrB = em.thr[tB];
   }
+  // Lanes of groups 0 and 2 own the scores of token A and token B (the
+  // epilogue leaves A's in lanes 0..31 and B's in 32..63): their position
+  // bound, threshold and output row or candidate slots.
+  const bool owner = g == 0 || g == 2;
+  const bool lane_b = g >= 2;
+  const int my_pos = lane_b ? posB : posA;
+  const float my_thr = lane_b ? thrB : thrA;
+  const int my_t = (lane_b && hasB) ? tB : tA;
+  float* my_row = nullptr;
+  if constexpr (MODE != kEmit) my_row = scores + int64_t(my_t) * ld;
+  // emit pass: candidates of this chunk so far (wave-uniform), and this lane's
+  // token's LDS candidate row
+  int cntA = 0, cntB = 0;
+  const int my_li = 2 * pair + ((lane_b && hasB) ? 1 : 0);
 
   // Page staging: 1024 16-byte pieces per page, 4 per thread, coalesced.
   auto page_src = [&](int pg) -> const u32x4* {
-    int id = page_table[int64_t(b) * pt_stride + pg];
+    int id = page_table[int64_t(b) * pt_stride + pg * kStride];
     id = min(max(id, 0), num_pages - 1);
     return reinterpret_cast<const u32x4*>(keys + int64_t(id) * kPageKeysBf16);
   };
   // two register stages: page pg+1 is in flight in one while page pg+2 is
-  // requested into the other (the stages alternate, so the loop is unrolled by 2)
+  // requested into the other
   u32x4 pa[4], pb[4];
   auto load_page = [&](u32x4 (&pre)[4], int pg) {
     const u32x4* src = page_src(pg);
@@ -118,56 +160,192 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int piece = tid + kThreads * i;
-      const int row = piece >> 4, col = (piece & 15) * 8;
-      *reinterpret_cast<u32x4*>(&lds[buf][row * kKeyStride + col]) = pre[i];
+      const int row = piece >> 4, chunk = (piece & 15) ^ (row & 15);
+      *reinterpret_cast<u32x4*>(&lds[buf][row * kRowBf16 + chunk * 8]) = pre[i];
     }
   };
 
+  // The memory schedule keeps every step straight-line, so the compiler's
+  // wait before staging a page counts exactly the four younger prefetch
+  // loads: prefetches are unconditional (past the range they repeat the last
+  // page), the idle LDS buffer is always written, and a step's outputs are
+  // held in registers and stored at the start of the next step, before its
+  // prefetch.
   load_page(pa, page_begin);
-  if (page_begin + 1 < page_end) load_page(pb, page_begin + 1);
+  load_page(pb, min(page_begin + 1, page_end - 1));
   store_page(pa, 0);
   __syncthreads();
   int cur = 0;
-  for (int pg = page_begin; pg < page_end; ++pg) {
-    // pb holds page pg+1 (if any) when an even step starts, pa when an odd one does
-    const bool odd = ((pg - page_begin) & 1) != 0;
-    const bool more = pg + 1 < page_end;
-    if (pg + 2 < page_end) {
-      if (odd) load_page(pb, pg + 2); else load_page(pa, pg + 2);
-    }
-    if (wave_active) {
-      const int pos0 = pg * DSA_PAGE_TOKENS;
-      for (int nb = sub; nb < 4; nb += nsub) {
-        const uint16_t* krow = &lds[cur][(nb * 16 + c) * kKeyStride + 8 * g];
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+  // scores of the last computed page (not the emit pass, which writes its
+  // candidates to LDS at once): the value of block slot k (block sub + k*nsub)
+  // and the page's first position / output column (held_pos0 < 0: nothing held)
+  float held[4];
+  int held_pos0 = -1, held_col0 = 0;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = dsa::as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * ks));
-          accA = dsa::mfma16x16x32(dsa::as_bf16x8(qa[ks]), kf, accA);
-          if (hasB) accB = dsa::mfma16x16x32(dsa::as_bf16x8(qb[ks]), kf, accB);
-        }
-        float sA = 0.f, sB = 0.f;
+  for (int k = 0; k < 4; ++k) held[k] = 0.f;
+  // scores (or candidates) of page pg, read from LDS buffer `cur`
+  auto compute_page = [&](int pg) {
+    const int pos0 = pg * kStride * DSA_PAGE_TOKENS;
+    // output column of the page's first position: the position itself, or
+    // in the sample pass the sample index (64 per sampled page)
+    const int col0 = MODE == kSample ? pg * DSA_PAGE_TOKENS : pos0;
+    // row nb*16 + c, dims 32ks + 8g.. (chunk 4ks + g, stored at (4ks + g) ^ c)
+    const uint16_t* kbase = &lds[cur][c * kRowBf16];
+    // one 16-position block: both tokens' dots (token B's are zero when the
+    // wave has one token) and the 16-head epilogue
+    auto block = [&](int k, int nb) {
+      const uint16_t* krow = kbase + nb * 16 * kRowBf16;
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sA = fmaf(wa[j], fmaxf(accA[j], 0.f), sA);
-          sB = fmaf(wb[j], fmaxf(accB[j], 0.f), sB);
-        }
-        sA = dsa::rows4_sum(sA);   // integer-valued: exact in any order
-        sB = dsa::rows4_sum(sB);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = dsa::as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * ((4 * ks + g) ^ c)));
+        accA = dsa::mfma16x16x32(dsa::as_bf16x8(qa[ks]), kf, accA);
+        accB = dsa::mfma16x16x32(dsa::as_bf16x8(qb[ks]), kf, accB);
+      }
+      // lanes 0..31: token A's scores, lanes 32..63: token B's; lanes of
+      // groups 0 and 2 own position c of the block
+      const float sc = dsa::index_score2(accA, wa, accB, wb);
+      if constexpr (MODE != kEmit) held[k] = sc;
+      if constexpr (MODE == kEmit) {
+        // slots follow the ballot order, i.e. position order
         const int p = pos0 + nb * 16 + c;
-        if (g == 0 && p <= posA) scores[int64_t(tA) * ld + p] = sA;
-        if (g == 1 && hasB && p <= posB) scores[int64_t(tB) * ld + p] = sB;
+        const bool cand = owner && p <= my_pos && sc >= my_thr;
+        const uint64_t m = __ballot(cand);
+        const uint32_t mA = uint32_t(m) & 0xFFFFu, mB = uint32_t(m >> 32) & 0xFFFFu;
+        // candidates below this lane in the ballot, minus token A's for B lanes
+        const int below = int(__builtin_amdgcn_mbcnt_hi(mB, __builtin_amdgcn_mbcnt_lo(mA, 0u)));
+        const int slot = (lane_b ? cntB - __popc(mA) : cntA) + below;
+        // LDS writes need no deferral (they do not count against the loads)
+        if (cand && slot < em.cap) {
+          cand_v[my_li * kCandLds + slot] = sc;
+          cand_p[my_li * kCandLds + slot] = uint16_t(p - p_begin);
+        }
+        cntA += __popc(mA);
+        cntB += __popc(mB);
+      }
+    };
+    if (nsub == 1) {
+      block(0, 0);
+      block(1, 1);
+      block(2, 2);
+      block(3, 3);
+    } else if (nsub == 2) {
+      block(0, sub);
+      block(1, sub + 2);
+    } else {
+      block(0, sub);
+    }
+    held_pos0 = pos0;
+    held_col0 = col0;
+  };
+  // stores the held outputs (wave-uniform: held_pos0 is the same in all lanes)
+  auto flush = [&]() {
+    if (held_pos0 < 0) return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < 4 / nsub) {
+        const int nb = sub + k * nsub;
+        const int p = held_pos0 + nb * 16 + c;
+        if constexpr (MODE != kEmit) {
+          if (owner && p <= my_pos) my_row[held_col0 + nb * 16 + c] = held[k];
+        }
       }
     }
-    if (more) {
-      if (odd) store_page(pa, cur ^ 1); else store_page(pb, cur ^ 1);
-    }
+    held_pos0 = -1;
+  };
+  // One page step: store the previous page's outputs, request page pg+2 into
+  // `fill`, compute page pg, stage page pg+1 (held in `next`) into the other
+  // LDS buffer.  Two steps per trip with the register stages swapped, so each
+  // stage is a fixed register set (a runtime choice between them makes the
+  // compiler wait for the loads right after issuing them).
+  auto step = [&](int pg, u32x4 (&next)[4], u32x4 (&fill)[4]) {
+    flush();
+    load_page(fill, min(pg + 2, page_end - 1));
+    if (wave_active) compute_page(pg);
+    store_page(next, cur ^ 1);
     __syncthreads();
     cur ^= 1;
+  };
+  int pg = page_begin;
+  for (; pg + 1 < page_end; pg += 2) {
+    step(pg, pb, pa);
+    step(pg + 1, pa, pb);
+  }
+  if (pg < page_end) step(pg, pb, pa);
+  flush();
+  if constexpr (MODE == kEmit) {
+    // each wave writes out its own tokens' LDS slots (the flushes above were
+    // its own LDS writes); the count may exceed em.cap: the selection treats
+    // that chunk as overflowed
+    if (wave_active) {
+      for (int side = 0; side < (hasB ? 2 : 1); ++side) {
+        const int li = 2 * pair + side;
+        const int cnt = side ? cntB : cntA;
+        const int n = min(cnt, em.cap);
+        const int64_t base = (int64_t(side ? tB : tA) * em.nch + chunk) * em.cap;
+        for (int s2 = lane; s2 < n; s2 += 64) {
+          em.val[base + s2] = cand_v[li * kCandLds + s2];
+          em.pos[base + s2] = p_begin + int(cand_p[li * kCandLds + s2]);
+        }
+        if (lane == 0) em.count[int64_t(side ? tB : tA) * em.nch + chunk] = cnt;
+      }
+    }
   }
 }
 
+// Workgroup = unit (chunk blockIdx.x, request blockIdx.y, query block
+// blockIdx.z).  (A persistent grid with static unit assignment measured
+// slower: it loses the dispatcher's balancing of uneven units.)
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 4) void index_kernel(
+    const uint16_t* __restrict__ keys, int num_pages, const int32_t* __restrict__ page_table,
+    int pt_stride, const int32_t* __restrict__ q_offsets, const int32_t* __restrict__ tok_pos,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, float* __restrict__ scores,
+    int64_t ld, int max_ctx, int num_tokens, dsa::IndexEmit em) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][DSA_PAGE_TOKENS * kRowBf16];
+  // emit pass: each token's candidates of the chunk (score, position - chunk
+  // start), written to memory once at the end
+  __shared__ float cand_v[MODE == kEmit ? kQB * kCandLds : 1];
+  __shared__ uint16_t cand_p[MODE == kEmit ? kQB * kCandLds : 1];
+  index_unit<MODE>(keys, num_pages, page_table, pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld,
+                   max_ctx, num_tokens, em, lds, cand_v, cand_p, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 }  // namespace
+
+namespace dsa {
+
+dsa_status launch_index(int mode, const dsa_pool* pool, const int32_t* page_table,
+                        int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                        int32_t max_q, const int32_t* tok_pos, int32_t num_tokens,
+                        int32_t max_ctx, const uint16_t* q_idx, const float* w, float* scores,
+                        int64_t ld, const IndexEmit* em, void* stream) {
+  // the sample pass has one (sample) page per 32 logical pages
+  const int64_t pages = (int64_t(max_ctx) + DSA_PAGE_TOKENS - 1) / DSA_PAGE_TOKENS;
+  const int64_t units = mode == kSample ? (pages + kSampleStride - 1) / kSampleStride : pages;
+  const int64_t per = mode == kSample ? kSampleChunkPages : kChunkPages;
+  const int64_t chunks = (units + per - 1) / per;
+  const int64_t qblocks = (int64_t(max_q) + kQB - 1) / kQB;
+  if (chunks > 0x7fffffff || num_reqs > 65535 || qblocks > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: batch exceeds the launch grid limits");
+  const uint16_t* keys =
+      reinterpret_cast<const uint16_t*>(pool->base + pool->layout.index_plane_offset);
+  const dim3 grid{unsigned(chunks), unsigned(num_reqs), unsigned(qblocks)};
+  const IndexEmit none{nullptr, nullptr, nullptr, nullptr, 0, 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto go = [&](auto kernel, const IndexEmit& e) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, st, keys, pool->num_pages, page_table,
+                       pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld, max_ctx, num_tokens, e);
+  };
+  if (mode == kScores) go(index_kernel<kScores>, none);
+  else if (mode == kSample) go(index_kernel<kSample>, none);
+  else go(index_kernel<kEmit>, *em);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, std::string("indexer: launch failed: ") + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace dsa
 
 extern "C" dsa_status dsa_index_scores(const dsa_pool* pool, const int32_t* page_table,
                                        int32_t pt_stride, const int32_t* q_offsets,
@@ -186,19 +364,6 @@ extern "C" dsa_status dsa_index_scores(const dsa_pool* pool, const int32_t* page
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: q_idx/scores must be 16-byte aligned");
   if (ld < max_ctx || ld % 4 != 0)
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: need ld >= max_ctx and ld % 4 == 0");
-  const int64_t chunks = (int64_t(max_ctx) + kChunkPages * DSA_PAGE_TOKENS - 1) /
-                         (kChunkPages * DSA_PAGE_TOKENS);
-  const int64_t qblocks = (int64_t(max_q) + kQB - 1) / kQB;
-  if (chunks > 0x7fffffff || num_reqs > 65535 || qblocks > 65535)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores: batch exceeds the launch grid limits");
-  const uint16_t* keys =
-      reinterpret_cast<const uint16_t*>(pool->base + pool->layout.index_plane_offset);
-  const dim3 grid{unsigned(chunks), unsigned(num_reqs), unsigned(qblocks)};
-  hipLaunchKernelGGL(index_scores_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     keys, pool->num_pages, page_table, pt_stride, q_offsets, tok_pos, q_idx, w,
-                     scores, ld, max_ctx, num_tokens);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return dsa::fail(DSA_ERR_HIP, std::string("dsa_index_scores: launch failed: ") + hipGetErrorString(e));
-  return dsa::ok();
+  return dsa::launch_index(kScores, pool, page_table, pt_stride, q_offsets, num_reqs, max_q, tok_pos,
+                           num_tokens, max_ctx, q_idx, w, scores, ld, nullptr, stream);
 }

@@ -34,6 +34,34 @@ dsa_status check_batch(const dsa_pool* pool, const int32_t* page_table, int32_t 
                        const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
                        int32_t num_tokens, const char* who);
 
+// Indexer geometry shared by the indexer and the fused top-k host code.
+constexpr int32_t kIndexChunkPages = 8;     // pages per indexer workgroup (512 positions)
+constexpr int32_t kIndexChunk = kIndexChunkPages * 64;
+constexpr int32_t kIndexSampleStride = 32;  // sample pass: logical pages 0, 32, 64, ...
+constexpr int32_t kIndexMaxCap = 128;       // emit pass: most candidate slots per token and chunk
+
+// Candidate output of the indexer's emit pass: for token t and chunk j (512
+// positions), the scores >= thr[t], in position order, at slots
+// [(t*nch + j)*cap, +cap), and their number (possibly > cap) in
+// count[t*nch + j].
+struct IndexEmit {
+  const float* thr;
+  float* val;
+  int32_t* pos;
+  int32_t* count;
+  int32_t nch, cap;
+};
+
+// Launches the indexer: mode 0 writes scores[t*ld + p]; mode 1 (sample pass)
+// writes scores[t*ld + 64*s + x] for position 64*32*s + x; mode 2 emits
+// candidates into *em (scores unused).  Arguments are those of
+// dsa_index_scores, already validated.
+dsa_status launch_index(int mode, const dsa_pool* pool, const int32_t* page_table,
+                        int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                        int32_t max_q, const int32_t* tok_pos, int32_t num_tokens,
+                        int32_t max_ctx, const uint16_t* q_idx, const float* w, float* scores,
+                        int64_t ld, const IndexEmit* em, void* stream);
+
 // Top-k staging geometry (host copy of what the kernels assume).
 constexpr int32_t kTopkSeg = 65536;      // positions one workgroup selects from
 constexpr int32_t kTopkMaxK = 16384;

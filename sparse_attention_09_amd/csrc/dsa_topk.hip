@@ -28,10 +28,15 @@
 // contained in the union of the segments' top-k.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace {
+
+using dsa::f32x4;
+using dsa::u32x4;
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
@@ -45,7 +50,7 @@ constexpr int kCap = 4096;                     // threshold-bin candidates kept 
 
 static_assert(kSeg == dsa::kTopkSeg, "segment size must match the host side");
 
-enum Mode { kDirect = 0, kSegment = 1, kMerge = 2 };
+enum Mode { kDirect = 0, kSegment = 1, kMerge = 2, kFallback = 3 };
 
 struct Smem {
   uint32_t hist[kBins];
@@ -120,34 +125,104 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return v;
 }
 
+// Indexer inputs of the exact fallback of the fused path (which recomputes a
+// token's scores instead of reading them).
+struct IndexIn {
+  const uint16_t* keys;         // indexer key plane, [page][64][128] bf16
+  int num_pages;
+  const int32_t* page_table;
+  int pt_stride;
+  const int32_t* q_offsets;
+  int num_reqs;
+  const uint16_t* q_idx;        // [T][16][128] bf16
+  const float* w;               // [T][16]
+};
+
+// The score bits of positions 1024*i + tid (i < kEPT) of token t, computed
+// like the indexer kernel: wave v takes the 64 positions (one page) starting
+// at 1024*i + 64*v; its four 16-position MFMA blocks use the same operand
+// layouts, accumulation order and epilogue as the indexer, so the bits match.
+// Positions at or past n are left 0 (masked by the caller).
+__device__ __forceinline__ void fallback_scores(uint32_t (&key)[kEPT], const IndexIn& f, int t, int n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  int lo = 0, hi = f.num_reqs;   // request b with q_offsets[b] <= t < q_offsets[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (f.q_offsets[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  u32x4 q[4];
+  float wv[4];
+  const u32x4* qs = reinterpret_cast<const u32x4*>(f.q_idx + (int64_t(t) * DSA_IDX_HEADS + c) * DSA_IDX_DIM);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) q[ks] = qs[ks * 4 + g];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wv[j] = f.w[int64_t(t) * DSA_IDX_HEADS + 4 * g + j];
+#pragma unroll
+  for (int i = 0; i < kEPT; ++i) {
+    const int p0 = kThreads * i + 64 * wave;
+    const int lp = p0 / DSA_PAGE_TOKENS;
+    float v = 0.f;
+    if (p0 < n && lp < f.pt_stride) {   // wave-uniform
+      int id = f.page_table[int64_t(b) * f.pt_stride + lp];
+      id = min(max(id, 0), f.num_pages - 1);
+      const uint16_t* page = f.keys + int64_t(id) * DSA_PAGE_TOKENS * DSA_IDX_DIM;
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const u32x4* krow = reinterpret_cast<const u32x4*>(page + (16 * b4 + c) * DSA_IDX_DIM) + g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = dsa::mfma16x16x32(dsa::as_bf16x8(q[ks]), dsa::as_bf16x8(krow[4 * ks]), acc);
+        const float sc = dsa::index_score(acc, wv);
+        if (g == b4) v = sc;
+      }
+    }
+    key[i] = __float_as_uint(v);
+  }
+}
+
+struct RowArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* tok_pos;
+  int max_ctx, k, nseg, kc;
+  float* cand_val;
+  int32_t* cand_pos;
+  int32_t* idx_out;
+};
+
+// Selects the top-k of one row: token t's visible scores (kDirect), segment
+// seg of them (kSegment), the segments' candidates (kMerge), or the scores
+// recomputed from the indexer inputs (kFallback).  Contains barriers; every
+// thread of the workgroup calls it with the same row.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void topk_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ tok_pos,
-    int max_ctx, int k, int nseg, int kc, float* __restrict__ cand_val,
-    int32_t* __restrict__ cand_pos, int32_t* __restrict__ idx_out) {
-  __shared__ Smem sm;
+__device__ __forceinline__ void topk_row(Smem& sm, const RowArgs& a, int t, int seg, const IndexIn& f) {
+  const float* __restrict__ scores = a.scores;
+  const int64_t ld = a.ld;
+  const int max_ctx = a.max_ctx, k = a.k, nseg = a.nseg, kc = a.kc;
+  float* __restrict__ cand_val = a.cand_val;
+  int32_t* __restrict__ cand_pos = a.cand_pos;
+  int32_t* __restrict__ idx_out = a.idx_out;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
   // ---- row geometry
-  int t, n, base = 0;
-  const float* vals;
+  int n, base = 0;
+  const float* vals = nullptr;
   const int32_t* vpos = nullptr;  // merge mode: candidate positions
   if (MODE == kSegment) {
-    t = blockIdx.y;
-    base = blockIdx.x * kSeg;
-    const int vis = min(tok_pos[t], max_ctx - 1) + 1;
+    base = seg * kSeg;
+    const int vis = min(a.tok_pos[t], max_ctx - 1) + 1;
     n = max(0, min(vis - base, kSeg));
     vals = scores + int64_t(t) * ld + base;
   } else if (MODE == kMerge) {
-    t = blockIdx.x;
     n = nseg * kc;
     vals = cand_val + int64_t(t) * n;
     vpos = cand_pos + int64_t(t) * n;
   } else {
-    t = blockIdx.x;
-    n = max(0, min(tok_pos[t], max_ctx - 1) + 1);
-    vals = scores + int64_t(t) * ld;
+    n = max(0, min(a.tok_pos[t], max_ctx - 1) + 1);
+    if (MODE == kDirect) vals = scores + int64_t(t) * ld;
   }
 
   for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
@@ -159,10 +234,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   uint32_t key[kEPT];
   const int cnt = n > tid ? (n - tid + kThreads - 1) / kThreads : 0;
   const int last = max(n - 1, 0);
+  if constexpr (MODE == kFallback) {
+    fallback_scores(key, f, t, n);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) {
-    const int e = min(kThreads * i + tid, last);
-    key[i] = __float_as_uint(vals[e]);
+    for (int i = 0; i < kEPT; ++i) {
+      const int e = min(kThreads * i + tid, last);
+      key[i] = __float_as_uint(vals[e]);
+    }
   }
   uint32_t my_valid = 0;
 #pragma unroll
@@ -317,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     x &= x - 1;
     const int e = 64 * tid + bit;
     if (MODE == kSegment) {
-      const int64_t o = (int64_t(t) * nseg + blockIdx.x) * kc + out;
+      const int64_t o = (int64_t(t) * nseg + seg) * kc + out;
       cand_val[o] = vals[e];
       cand_pos[o] = base + e;
     } else if (MODE == kMerge) {
@@ -329,12 +408,322 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   }
   for (int i = int(total) + tid; i < limit; i += kThreads) {
     if (MODE == kSegment) {
-      const int64_t o = (int64_t(t) * nseg + blockIdx.x) * kc + i;
+      const int64_t o = (int64_t(t) * nseg + seg) * kc + i;
       cand_val[o] = 0.f;
       cand_pos[o] = -1;
     } else {
       idx_out[int64_t(t) * k + i] = -1;
     }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void topk_kernel(RowArgs a) {
+  __shared__ Smem sm;
+  const IndexIn none{nullptr, 0, nullptr, 0, nullptr, 0, nullptr, nullptr};
+  topk_row<MODE>(sm, a, MODE == kSegment ? int(blockIdx.y) : int(blockIdx.x), blockIdx.x, none);
+}
+
+// ===================================================================== fused
+// Fused indexer + top-k for rows of at most 65,536 positions (no score
+// matrix):
+//   1. the indexer's sample pass scores logical pages 0, 32, 64, ...;
+//   2. threshold_kernel: per token, the r-th largest sampled score, r chosen
+//      so that about `target` positions of the row should reach it;
+//   3. the indexer's emit pass keeps only positions scoring at least the
+//      threshold, in position order, in fixed slots per (token, 512-chunk);
+//   4. select_kernel: when no chunk overflowed and at least k candidates
+//      exist, the exact top-k of the row lies among them (every other
+//      position scores strictly below every candidate, so it cannot beat or
+//      tie the k-th largest), and selecting among them under the same rule
+//      (score desc, position asc) gives the same answer; otherwise the token
+//      is listed;
+//   5. fallback_kernel: listed tokens recompute their row into registers and
+//      run the one-workgroup selection above.
+
+constexpr int kSmallThreads = 256;
+constexpr int kMaxSamples = 2048;     // sample columns of a 65,536-position row
+constexpr int kSelMax = 6144;         // candidates one selection workgroup holds
+constexpr int kMaxChunks = kSeg / dsa::kIndexChunk;
+constexpr int kRankSlack = 8;         // extra sample rank: fewer short-of-k rows
+
+struct Sel {
+  uint32_t hist[2][256];
+  uint32_t wtmp[4][4];
+  uint32_t digit, above;
+};
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, uint32_t(__shfl_xor(v, off)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, uint32_t(__shfl_xor(v, off)));
+  return v;
+}
+
+// Exclusive scan over a 256-thread workgroup; *total gets the sum.  Barriers.
+__device__ __forceinline__ uint32_t scan256(uint32_t v, Sel& s, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v, lane);
+  if (lane == 63) s.wtmp[wave][0] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = s.wtmp[i][0];
+    before += i < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
+// Minimum and maximum of keys (lo/hi per thread) and a count sum over a
+// 256-thread workgroup.  Barriers.
+__device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint32_t n,
+                                          uint32_t* glo, uint32_t* ghi, uint32_t* gn) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  n = wave_sum(n);
+  if (lane == 0) {
+    s.wtmp[wave][1] = lo;
+    s.wtmp[wave][2] = hi;
+    s.wtmp[wave][3] = n;
+  }
+  __syncthreads();
+  lo = s.wtmp[0][1];
+  hi = s.wtmp[0][2];
+  n = s.wtmp[0][3];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    lo = min(lo, s.wtmp[i][1]);
+    hi = max(hi, s.wtmp[i][2]);
+    n += s.wtmp[i][3];
+  }
+  __syncthreads();
+  *glo = lo;
+  *ghi = hi;
+  *gn = n;
+}
+
+// k-th largest of a key multiset spread over a 256-thread workgroup
+// (1 <= k <= its size; every key in [kmin, kmax]).  Radix selection on
+// d = key - kmin, 8-bit digits from the top bit of kmax - kmin down, so the
+// first digit already spreads the keys.  `each(f)` calls f on every key the
+// calling thread holds.  Returns the key; *r_out gets how many keys equal to
+// it belong to the k largest.  Barriers.
+template <class Each>
+__device__ __forceinline__ uint32_t radix_select256(Sel& s, uint32_t k_rem, uint32_t kmin,
+                                                    uint32_t kmax, Each each, uint32_t* r_out) {
+  const int tid = threadIdx.x;
+  const uint32_t span = kmax - kmin;
+  if (span == 0) {
+    *r_out = k_rem;
+    return kmin;
+  }
+  const int passes = (32 - __clz(span) + 7) / 8;
+  uint32_t prefix = 0;   // decided high digits of d
+  s.hist[0][tid] = 0;
+  __syncthreads();
+  for (int pass = 0; pass < passes; ++pass) {
+    const int sh = 8 * (passes - 1 - pass);
+    uint32_t* h = s.hist[pass & 1];
+    s.hist[(pass + 1) & 1][tid] = 0;   // the next pass's histogram
+    each([&](uint32_t key) {
+      const uint32_t d = (key - kmin) >> sh;
+      if ((d >> 8) == prefix) atomicAdd(&h[d & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < 64) {
+      // lane l scans bins 255-4l .. 252-4l (top down)
+      uint32_t hb[4], local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hb[j] = h[255 - 4 * tid - j];
+        local += hb[j];
+      }
+      const uint32_t inc = wave_incl_scan(local, tid);
+      uint32_t acc = inc - local;
+      if (acc < k_rem && k_rem <= inc) {
+        for (int j = 0; j < 4; ++j) {
+          if (acc + hb[j] >= k_rem) {
+            s.digit = uint32_t(255 - 4 * tid - j);
+            s.above = acc;
+            break;
+          }
+          acc += hb[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << 8) | s.digit;
+    k_rem -= s.above;
+  }
+  *r_out = k_rem;
+  return kmin + prefix;
+}
+
+// One workgroup per token.  Sample column q lies at position
+// 2048*(q/64) + q%64.  Writes the token's threshold score (-inf: keep every
+// position).  Also resets the fallback list (block 0).
+__global__ __launch_bounds__(kSmallThreads) void threshold_kernel(
+    const float* __restrict__ samples, int ls, const int32_t* __restrict__ tok_pos, int max_ctx,
+    int k, int target, float* __restrict__ thr, int32_t* __restrict__ nflag) {
+  __shared__ Sel s;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (t == 0 && tid == 0) *nflag = 0;
+  const int vis = max(0, min(tok_pos[t], max_ctx - 1) + 1);
+  if (vis <= k) {          // the selection keeps the whole row
+    if (tid == 0) thr[t] = -__builtin_inff();
+    return;
+  }
+  constexpr int kPer = kMaxSamples / kSmallThreads;
+  uint32_t key[kPer];
+  bool ok[kPer];
+  uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + kSmallThreads * i;
+    const int p = dsa::kIndexSampleStride * DSA_PAGE_TOKENS * (q >> 6) + (q & 63);
+    ok[i] = q < ls && p < vis;
+    key[i] = ok[i] ? dsa::float_key(samples[int64_t(t) * ls + q]) : 0u;
+    nv += ok[i] ? 1u : 0u;
+    lo = ok[i] ? min(lo, key[i]) : lo;
+    hi = ok[i] ? max(hi, key[i]) : hi;
+  }
+  uint32_t kmin, kmax, ns;
+  minmax256(s, lo, hi, nv, &kmin, &kmax, &ns);
+  const int64_t r = (int64_t(target) * ns + vis - 1) / vis + kRankSlack;
+  if (r >= int64_t(ns)) {  // too few samples to cut anything: keep every position
+    if (tid == 0) thr[t] = -__builtin_inff();
+    return;
+  }
+  uint32_t rr;
+  const uint32_t tau = radix_select256(
+      s, uint32_t(r), kmin, kmax,
+      [&](auto&& f) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (ok[i]) f(key[i]);
+      },
+      &rr);
+  if (tid == 0) thr[t] = dsa::key_float(tau);
+}
+
+struct SelSmem {
+  uint32_t key[kSelMax];
+  uint16_t pos[kSelMax];      // rows are at most 65,536 positions
+  int32_t off[kMaxChunks];
+  Sel s;
+};
+
+// One workgroup per token: compacts its candidates into LDS (in position
+// order), selects exactly, writes the k positions ascending.  Rows of at
+// most k positions are written whole.  Tokens whose candidates cannot be
+// trusted go to the fallback list.
+__global__ __launch_bounds__(kSmallThreads) void select_kernel(
+    const int32_t* __restrict__ tok_pos, int max_ctx, int k, const int32_t* __restrict__ count,
+    const float* __restrict__ cval, const int32_t* __restrict__ cpos, int nch, int cap,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ nflag, int32_t* __restrict__ flag_list) {
+  __shared__ SelSmem sm;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int vis = max(0, min(tok_pos[t], max_ctx - 1) + 1);
+  int32_t* out = idx_out + int64_t(t) * k;
+  if (vis <= k) {
+    for (int i = tid; i < k; i += kSmallThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
+  const int nch_t = (vis + dsa::kIndexChunk - 1) / dsa::kIndexChunk;
+  int c = 0;
+  bool over = false;
+  if (tid < nch_t) {
+    c = count[int64_t(t) * nch + tid];
+    over = c > cap || c < 0;
+  }
+  uint32_t n;
+  const uint32_t o = scan256(over ? 0u : uint32_t(c), sm.s, &n);
+  if (tid < nch_t) sm.off[tid] = int32_t(o);
+  const bool bad = __syncthreads_or(over) || n < uint32_t(k) || n > uint32_t(kSelMax);
+  if (bad) {
+    if (tid == 0) flag_list[atomicAdd(nflag, 1)] = t;
+    return;
+  }
+  const int N = int(n);
+  // compaction, all loads of a thread in flight together: candidate q is slot
+  // q - off[j] of the chunk j holding it
+  constexpr int kPer = kSelMax / kSmallThreads;
+  int64_t src[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int q = kSmallThreads * u + tid;
+    int j = 0;
+#pragma unroll
+    for (int step = kMaxChunks / 2; step > 0; step >>= 1) {
+      const int m = j + step;
+      if (m < nch_t && sm.off[m] <= q) j = m;
+    }
+    src[u] = q < N ? (int64_t(t) * nch + j) * cap + (q - sm.off[j]) : -1;
+  }
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (src[u] >= 0) {
+      const uint32_t key = dsa::float_key(cval[src[u]]);
+      const int q = kSmallThreads * u + tid;
+      sm.key[q] = key;
+      sm.pos[q] = uint16_t(cpos[src[u]]);
+      lo = min(lo, key);
+      hi = max(hi, key);
+    }
+  }
+  uint32_t kmin, kmax, unused;
+  minmax256(sm.s, lo, hi, 0u, &kmin, &kmax, &unused);   // its barriers publish sm.key/pos
+  uint32_t r;
+  const uint32_t tau = radix_select256(
+      sm.s, uint32_t(k), kmin, kmax,
+      [&](auto&& f) {
+        for (int q = tid; q < N; q += kSmallThreads) f(sm.key[q]);
+      },
+      &r);
+  // thread i owns candidates [E*i, E*i + E): equal keys kept lowest position first
+  const int E = (N + kSmallThreads - 1) / kSmallThreads;
+  const int q0 = min(tid * E, N), q1 = min(q0 + E, N);
+  uint32_t gt = 0, eq = 0;
+  for (int q = q0; q < q1; ++q) {
+    const uint32_t key = sm.key[q];
+    gt += key > tau ? 1u : 0u;
+    eq += key == tau ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = scan256(eq, sm.s, &tot);
+  uint32_t take = eq_before < r ? min(eq, r - eq_before) : 0u;
+  uint32_t w = scan256(gt + take, sm.s, &tot);
+  for (int q = q0; q < q1; ++q) {
+    const uint32_t key = sm.key[q];
+    bool keep = key > tau;
+    if (key == tau && take > 0) {
+      keep = true;
+      --take;
+    }
+    if (keep && w < uint32_t(k)) out[w++] = int32_t(sm.pos[q]);   // exactly k are kept
+  }
+}
+
+// Persistent over the fallback list (every workgroup leaves once the list is
+// exhausted).
+__global__ __launch_bounds__(kThreads) void fallback_kernel(RowArgs a, IndexIn f,
+                                                            const int32_t* __restrict__ nflag,
+                                                            const int32_t* __restrict__ flag_list) {
+  __shared__ Smem sm;
+  const int n = *nflag;
+  for (int li = blockIdx.x; li < n; li += gridDim.x) {
+    topk_row<kFallback>(sm, a, flag_list[li], 0, f);
+    __syncthreads();
   }
 }
 
@@ -357,8 +746,8 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* t
     return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_topk: too many long rows for one launch");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (max_ctx <= kSeg) {
-    hipLaunchKernelGGL(topk_kernel<kDirect>, dim3(num_tokens), dim3(kThreads), 0, st, scores, ld,
-                       tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx);
+    const RowArgs a{scores, ld, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
+    hipLaunchKernelGGL(topk_kernel<kDirect>, dim3(num_tokens), dim3(kThreads), 0, st, a);
   } else {
     const int nseg = dsa::topk_num_segments(max_ctx);
     const int kc = (k + 3) & ~3;
@@ -373,13 +762,115 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* t
     float* cv = static_cast<float*>(workspace);
     int32_t* cp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                              size_t(num_tokens) * nseg * kc * 4);
-    hipLaunchKernelGGL(topk_kernel<kSegment>, dim3(nseg, num_tokens), dim3(kThreads), 0, st, scores,
-                       ld, tok_pos, max_ctx, k, nseg, kc, cv, cp, nullptr);
-    hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(num_tokens), dim3(kThreads), 0, st, scores, ld,
-                       tok_pos, max_ctx, k, nseg, kc, cv, cp, idx);
+    const RowArgs a{scores, ld, tok_pos, max_ctx, k, nseg, kc, cv, cp, idx};
+    hipLaunchKernelGGL(topk_kernel<kSegment>, dim3(nseg, num_tokens), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(num_tokens), dim3(kThreads), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dsa::fail(DSA_ERR_HIP, std::string("dsa_topk: launch failed: ") + hipGetErrorString(e));
+  return dsa::ok();
+}
+
+namespace {
+
+// Workspace of the fused path (byte offsets, each 256-aligned).  The fallback
+// counter sits at offset 0.
+struct FusedLayout {
+  size_t nflag, list, samples, thr, count, val, pos, total;
+  int ls, nch;
+};
+
+FusedLayout fused_layout(int64_t num_tokens, int32_t max_ctx, int32_t cap) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  FusedLayout L{};
+  const int64_t pages = (int64_t(max_ctx) + DSA_PAGE_TOKENS - 1) / DSA_PAGE_TOKENS;
+  const int64_t spages = (pages + dsa::kIndexSampleStride - 1) / dsa::kIndexSampleStride;
+  L.ls = int(spages * DSA_PAGE_TOKENS);
+  L.nch = int((int64_t(max_ctx) + dsa::kIndexChunk - 1) / dsa::kIndexChunk);
+  const size_t T = size_t(num_tokens);
+  size_t o = 0;
+  L.nflag = o; o += up(4);
+  L.list = o; o += up(4 * T);
+  L.samples = o; o += up(4 * T * size_t(L.ls));
+  L.thr = o; o += up(4 * T);
+  L.count = o; o += up(4 * T * size_t(L.nch));
+  L.val = o; o += up(4 * T * size_t(L.nch) * size_t(cap));
+  L.pos = o; o += up(4 * T * size_t(L.nch) * size_t(cap));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t dsa_index_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t cap) {
+  if (num_tokens <= 0 || max_ctx < 0 || max_ctx > kSeg || cap < 1 || cap > dsa::kIndexMaxCap) return 0;
+  return fused_layout(num_tokens, max_ctx, cap).total;
+}
+
+extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table,
+                                     int32_t pt_stride, const int32_t* q_offsets, int32_t num_reqs,
+                                     int32_t max_q, const int32_t* tok_pos, int32_t num_tokens,
+                                     int32_t max_ctx, const uint16_t* q_idx, const float* w,
+                                     int32_t k, int32_t cap, int32_t cand_target, int32_t* idx,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status s = dsa::check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
+                                  num_tokens, "dsa_index_topk");
+  if (s != DSA_OK) return s;
+  if (k < 1 || k > dsa::kTopkMaxK)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need 1 <= k <= 16384");
+  if (cap < 1 || cap > dsa::kIndexMaxCap || cand_target < 0)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need 1 <= cap <= 128 and cand_target >= 0");
+  if (max_q < 1 || max_ctx < 0)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need max_q >= 1 and max_ctx >= 0");
+  if (max_ctx > kSeg)
+    return dsa::fail(DSA_ERR_UNSUPPORTED,
+                     "dsa_index_topk: rows above 65,536 positions need dsa_index_scores + dsa_topk");
+  if (num_tokens == 0) return dsa::ok();
+  if (!q_idx || !w || !idx)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: q_idx, w and idx must be non-null");
+  if (!dsa::aligned(q_idx, 16) || !dsa::aligned(w, 4) || !dsa::aligned(idx, 4))
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: q_idx must be 16-byte aligned");
+  const FusedLayout L = fused_layout(num_tokens, max_ctx, cap);
+  if (!workspace || workspace_bytes < L.total)
+    return dsa::fail(DSA_ERR_WORKSPACE, "dsa_index_topk: workspace of " + std::to_string(L.total) +
+                                            " bytes required");
+  if (!dsa::aligned(workspace, 256))
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* nflag = reinterpret_cast<int32_t*>(ws + L.nflag);
+  int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
+  float* samples = reinterpret_cast<float*>(ws + L.samples);
+  float* thr = reinterpret_cast<float*>(ws + L.thr);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+  float* cval = reinterpret_cast<float*>(ws + L.val);
+  int32_t* cpos = reinterpret_cast<int32_t*>(ws + L.pos);
+  // default: about 2k candidates (within what one selection workgroup holds)
+  const int target = cand_target > 0 ? cand_target : std::min(2 * k, kSelMax - 1024);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (max_ctx > 0) {
+    s = dsa::launch_index(1, pool, page_table, pt_stride, q_offsets, num_reqs, max_q, tok_pos,
+                          num_tokens, max_ctx, q_idx, w, samples, L.ls, nullptr, stream);
+    if (s != DSA_OK) return s;
+  }
+  hipLaunchKernelGGL(threshold_kernel, dim3(num_tokens), dim3(kSmallThreads), 0, st, samples, L.ls,
+                     tok_pos, max_ctx, k, target, thr, nflag);
+  if (max_ctx > 0) {
+    const dsa::IndexEmit em{thr, cval, cpos, count, L.nch, cap};
+    s = dsa::launch_index(2, pool, page_table, pt_stride, q_offsets, num_reqs, max_q, tok_pos,
+                          num_tokens, max_ctx, q_idx, w, nullptr, 0, &em, stream);
+    if (s != DSA_OK) return s;
+  }
+  hipLaunchKernelGGL(select_kernel, dim3(num_tokens), dim3(kSmallThreads), 0, st, tok_pos, max_ctx,
+                     k, count, cval, cpos, L.nch, cap, idx, nflag, list);
+  const RowArgs a{nullptr, 0, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
+  const IndexIn f{reinterpret_cast<const uint16_t*>(pool->base + pool->layout.index_plane_offset),
+                  pool->num_pages, page_table, pt_stride, q_offsets, num_reqs, q_idx, w};
+  hipLaunchKernelGGL(fallback_kernel, dim3(std::min(num_tokens, 256)), dim3(kThreads), 0, st, a, f,
+                     nflag, list);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string("dsa_index_topk: launch failed: ") + hipGetErrorString(e));
   return dsa::ok();
 }

@@ -39,6 +39,7 @@ EXPORTS = [
     "dsa_pool_num_pages", "dsa_pool_kv_dtype",
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
     "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
+    "dsa_index_topk_workspace_bytes", "dsa_index_topk",
 ]
 
 
@@ -105,6 +106,9 @@ def lib() -> ctypes.CDLL:
                                      vp]),
             "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "dsa_kv_append": (i32, [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]),
+            "dsa_index_topk_workspace_bytes": (sz, [i32, i32, i32]),
+            "dsa_index_topk": (i32, [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, i32, i32, i32,
+                                     vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -259,6 +263,42 @@ def topk(scores: torch.Tensor, tok_pos: torch.Tensor, k: int, max_ctx: int,
     return idx
 
 
+FUSED_MAX_CTX = 65536      # longest row dsa_index_topk takes
+DEFAULT_CAP = 128          # candidate slots per token and 512-position chunk
+
+
+def index_topk_workspace_bytes(num_tokens: int, max_ctx: int, cap: int = DEFAULT_CAP) -> int:
+    return int(lib().dsa_index_topk_workspace_bytes(num_tokens, max_ctx, cap))
+
+
+def index_topk(pool: Pool, page_table, q_offsets, tok_pos, q_idx, w, max_q: int, max_ctx: int,
+               k: int, cap: int = DEFAULT_CAP, cand_target: int = 0,
+               idx: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused indexer + top-k: the idx of index_scores + topk without the score
+    matrix.  workspace[0:4] (int32) holds the number of tokens that took the
+    exact fallback once the call has run."""
+    dev = pool.device
+    T = tok_pos.numel()
+    B = q_offsets.numel() - 1
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(q_idx, "q_idx", torch.bfloat16, dev, (T, IDX_HEADS, IDX_DIM))
+    _need(w, "w", torch.float32, dev, (T, IDX_HEADS))
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, dev, (T, k))
+    need = index_topk_workspace_bytes(T, max_ctx, cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dsa_index_topk(pool.handle, _ptr(page_table), page_table.shape[-1], _ptr(q_offsets),
+                                B, max_q, _ptr(tok_pos), T, max_ctx, _ptr(q_idx), _ptr(w), k, cap,
+                                cand_target, _ptr(idx), _ptr(workspace), workspace.numel(),
+                                _stream(dev)))
+    return idx
+
+
 def sparse_mla_partial(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_scale: float,
                        kv_tile: int, num_splits: int, o_part=None, lse_part=None):
     dev = pool.device
@@ -347,11 +387,13 @@ class DsaPath:
     """The calls of one decode/prefill step, with their buffers allocated once
     for a fixed batch shape (so repeated steps allocate nothing).  With one
     KV split the attention runs as dsa_sparse_mla (final output directly, no
-    Combine); with several, as dsa_sparse_mla_partial + dsa_combine."""
+    Combine); with several, as dsa_sparse_mla_partial + dsa_combine.  Rows of
+    up to 65,536 positions select through dsa_index_topk (no score matrix)
+    unless select="scores"; longer ones through dsa_index_scores + dsa_topk."""
 
     def __init__(self, pool: Pool, page_table, q_offsets, tok_pos, max_q: int, max_ctx: int,
                  k: int, kv_tile: int = 0, num_splits: int = 0, sm_scale: Optional[float] = None,
-                 cu_count: int = 0):
+                 cu_count: int = 0, select: str = "auto", cap: int = DEFAULT_CAP):
         self.pool = pool
         self.page_table, self.q_offsets, self.tok_pos = page_table, q_offsets, tok_pos
         self.max_q, self.max_ctx, self.k = int(max_q), int(max_ctx), int(k)
@@ -360,11 +402,18 @@ class DsaPath:
         self.T = T
         self.plan = plan_partial(T, k, kv_tile, num_splits, cu_count)
         dev = pool.device
+        if select not in ("auto", "fused", "scores"):
+            raise ValueError("select must be auto, fused or scores")
+        self.fused_topk = select == "fused" or (select == "auto" and self.max_ctx <= FUSED_MAX_CTX)
+        self.cap = int(cap)
         self.ld = (max(max_ctx, 1) + 3) // 4 * 4
-        self.scores = torch.empty((T, self.ld), dtype=torch.float32, device=dev)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-        need = topk_workspace_bytes(T, max_ctx, k)
-        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+        self.scores = self.workspace = self.fused_ws = None
+        if self.fused_topk:
+            need = index_topk_workspace_bytes(T, self.max_ctx, self.cap)
+            self.fused_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        else:
+            self._alloc_scores()
         S = self.plan.splits
         self.fused = S == 1
         self.o_part = self.lse_part = None
@@ -373,12 +422,36 @@ class DsaPath:
         self.out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
 
+    def _alloc_scores(self):
+        dev = self.pool.device
+        self.scores = torch.empty((self.T, self.ld), dtype=torch.float32, device=dev)
+        need = topk_workspace_bytes(self.T, self.max_ctx, self.k)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+
     def index_scores(self, q_idx, w):
+        """Unfused form (score matrix allocated on first use for a fused path)."""
+        if self.scores is None:
+            self._alloc_scores()
         return index_scores(self.pool, self.page_table, self.q_offsets, self.tok_pos, q_idx, w,
                             self.max_q, self.max_ctx, self.scores, self.ld)
 
     def topk(self):
         return topk(self.scores, self.tok_pos, self.k, self.max_ctx, self.idx, self.workspace)
+
+    def index_topk(self, q_idx, w):
+        return index_topk(self.pool, self.page_table, self.q_offsets, self.tok_pos, q_idx, w,
+                          self.max_q, self.max_ctx, self.k, self.cap, 0, self.idx, self.fused_ws)
+
+    def select(self, q_idx, w):
+        """idx of this step's tokens, by whichever selection the path uses."""
+        if self.fused_topk:
+            return self.index_topk(q_idx, w)
+        self.index_scores(q_idx, w)
+        return self.topk()
+
+    def fallback_count(self) -> int:
+        """Tokens of the last fused selection that took the exact fallback."""
+        return int(self.fused_ws[:4].view(torch.int32).item()) if self.fused_topk else 0
 
     def _alloc_parts(self):
         T, S, dev = self.T, self.plan.splits, self.pool.device
@@ -404,6 +477,5 @@ class DsaPath:
         return self.combine()
 
     def step(self, q_idx, w, q):
-        self.index_scores(q_idx, w)
-        self.topk()
+        self.select(q_idx, w)
         return self.attend(q)

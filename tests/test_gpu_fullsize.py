@@ -17,12 +17,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _run(wl, kv_tile=0, num_splits=0, pool_tensor=None):
+def _run(wl, kv_tile=0, num_splits=0, select="scores"):
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     pool = dsa.Pool(wl.pool, wl.num_pages, wl.spec.kv_dtype)
     path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx,
                        wl.spec.k, kv_tile=kv_tile, num_splits=num_splits,
-                       sm_scale=wl.spec.sm_scale, cu_count=cus)
+                       sm_scale=wl.spec.sm_scale, cu_count=cus, select=select)
     out, lse = path.step(wl.q_idx, wl.w, wl.q)
     torch.cuda.synchronize()
     return path, out, lse
@@ -53,8 +53,9 @@ def _check_tokens(wl, path, out, lse, tokens):
     for t in tokens:
         pos = int(hv.tok_pos[t])
         ref = hv.token(t, path.plan.tile, path.plan.splits)
-        scores = path.scores[t, :pos + 1].cpu().numpy()
-        assert np.array_equal(scores, ref["scores"]), f"scores differ at token {t}"
+        if path.scores is not None:
+            scores = path.scores[t, :pos + 1].cpu().numpy()
+            assert np.array_equal(scores, ref["scores"]), f"scores differ at token {t}"
         assert np.array_equal(path.idx[t].cpu().numpy(), ref["idx"]), f"top-k differs at token {t}"
         check_attention(bf16_to_f64(out[t]), lse[t].cpu().numpy().astype(np.float64), ref["o"],
                         ref["lse"], f"token {t}")
@@ -132,4 +133,28 @@ def test_shared_prefix_fp8_full_tiles_and_pool_layouts():
     assert torch.equal(idx32, pd.idx)
     assert torch.equal(od, o_ref) and torch.equal(ld_, l_ref)
     del dup, pd, od, ld_
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["verify_fp8_64k", "prefill_fp8_32k"])
+def test_fused_select_full(name):
+    """The fused indexer + top-k (the default path for rows up to 65,536) at
+    full size: every token's indices equal the unfused calls' (which the tests
+    above pin to the oracle), sampled tokens equal the oracle's, and the
+    attention behind it stays within tolerance."""
+    wl = _gen(name)
+    path, out, lse = _run(wl, select="auto")
+    assert path.fused_topk
+    nfb = path.fallback_count()
+    say(f"[case] {name}: fused selection, {nfb} tokens took the fallback")
+    assert nfb == 0      # random scores: the sampled threshold leaves >= k candidates
+    _check_all_tokens(wl, path, out, lse)
+    idx_fused = path.idx.clone()
+    path.index_scores(wl.q_idx, wl.w)
+    path.topk()
+    torch.cuda.synchronize()
+    assert torch.equal(idx_fused, path.idx)
+    path.scores = None
+    _check_tokens(wl, path, out, lse, _sample(wl.num_tokens, 3, 4))
+    del wl, path, out, lse, idx_fused
     torch.cuda.empty_cache()

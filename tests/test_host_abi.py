@@ -189,6 +189,43 @@ def test_topk_workspace_bytes():
     assert L.dsa_topk_workspace_bytes(2, 70000, 5) == 2 * 2 * 8 * 8
 
 
+def test_index_topk_workspace_bytes():
+    L = dsa.lib()
+    T, cap = 1024, 128
+    # fallback counter, fallback list, samples (one page in 32: 32 x 64 columns),
+    # thresholds, counts per 512-chunk (128), candidate scores and positions
+    want = 256 + 4 * T + 4 * T * 2048 + 4 * T + 4 * T * 128 + 2 * (4 * T * 128 * cap)
+    assert L.dsa_index_topk_workspace_bytes(T, 65536, cap) == want
+    assert L.dsa_index_topk_workspace_bytes(T, 65537, cap) == 0     # rows too long
+    assert L.dsa_index_topk_workspace_bytes(T, 4096, 0) == 0
+    assert L.dsa_index_topk_workspace_bytes(T, 4096, 129) == 0
+    assert L.dsa_index_topk_workspace_bytes(0, 4096, 128) == 0
+
+
+def test_index_topk_validates_before_launch():
+    L = dsa.lib()
+    vp = ctypes.c_void_p
+    h = _raw_pool(4)
+    f = vp(FAKE)
+    need = L.dsa_index_topk_workspace_bytes(1, 256, 128)
+
+    def call(k=64, cap=128, target=0, max_ctx=256, ws=f, ws_bytes=need, T=1, pool=h):
+        return L.dsa_index_topk(pool, f, 4, f, 1, 1, f, T, max_ctx, f, f, k, cap, target, f, ws,
+                                ws_bytes, None)
+
+    assert call(pool=None) == 1
+    assert call(k=0) == 1
+    assert call(k=20000) == 1
+    assert call(cap=0) == 1 and call(cap=129) == 1
+    assert call(target=-1) == 1
+    assert call(max_ctx=65537) == 2
+    assert call(ws=None) == 4
+    assert call(ws_bytes=need - 1) == 4
+    assert call(ws=vp(FAKE + 16)) == 1
+    assert call(T=0) == 0
+    L.dsa_pool_destroy(h)
+
+
 def test_compute_calls_validate_before_launch():
     L = dsa.lib()
     vp = ctypes.c_void_p
