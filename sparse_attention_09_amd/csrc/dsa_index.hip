@@ -9,10 +9,15 @@
 // context, so the key stream dominates: each workgroup owns one request, up to
 // 8 of its query tokens (8 x 16 heads = 128 MFMA rows) and a chunk of 8 pages
 // (512 positions).  Keys are streamed page by page (16 KB) through a
-// double-buffered LDS stage with a register prefetch of the next page, and
-// every key read from HBM serves all the block's tokens and heads.  Dot
-// products run on the bf16 MFMA with fp32 accumulation; relu, the head
-// weights and the 16-head sum happen in registers and cross-lane shuffles.
+// double-buffered LDS stage with a two-stage register prefetch, and every key
+// read from HBM serves all the block's tokens and heads.  Dot products run on
+// the bf16 MFMA with fp32 accumulation; relu, the head weights and the 16-head
+// sum happen in registers and cross-lane swaps.
+//
+// Three modes share the kernel: scores (write every visible score), sample
+// (score logical pages 0, 32, 64, ... only) and emit (keep, per token and
+// chunk, the positions scoring at least a per-token threshold, in position
+// order) - the last two feed the fused top-k.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -586,12 +586,20 @@ __global__ __launch_bounds__(kSmallThreads) void threshold_kernel(
   uint32_t key[kPer];
   bool ok[kPer];
   uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
+  // loads unconditional (a column past the row reads column 0) so all are in
+  // flight at once
+  float sv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + kSmallThreads * i;
+    sv[i] = samples[int64_t(t) * ls + (q < ls ? q : 0)];
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = tid + kSmallThreads * i;
     const int p = dsa::kIndexSampleStride * DSA_PAGE_TOKENS * (q >> 6) + (q & 63);
     ok[i] = q < ls && p < vis;
-    key[i] = ok[i] ? dsa::float_key(samples[int64_t(t) * ls + q]) : 0u;
+    key[i] = ok[i] ? dsa::float_key(sv[i]) : 0u;
     nv += ok[i] ? 1u : 0u;
     lo = ok[i] ? min(lo, key[i]) : lo;
     hi = ok[i] ? max(hi, key[i]) : hi;
@@ -669,14 +677,25 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
     }
     src[u] = q < N ? (int64_t(t) * nch + j) * cap + (q - sm.off[j]) : -1;
   }
+  // loads unconditional (an unused slot reads the token's first slot) so all
+  // are in flight at once; LDS writes after
+  float v[kPer];
+  int32_t pv[kPer];
+  const int64_t first = int64_t(t) * nch * cap;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t a = src[u] >= 0 ? src[u] : first;
+    v[u] = cval[a];
+    pv[u] = cpos[a];
+  }
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     if (src[u] >= 0) {
-      const uint32_t key = dsa::float_key(cval[src[u]]);
+      const uint32_t key = dsa::float_key(v[u]);
       const int q = kSmallThreads * u + tid;
       sm.key[q] = key;
-      sm.pos[q] = uint16_t(cpos[src[u]]);
+      sm.pos[q] = uint16_t(pv[u]);
       lo = min(lo, key);
       hi = max(hi, key);
     }
