@@ -88,6 +88,39 @@ def time_kv_append(dsa, kv_dtype, dev, rows=32768, reps=20):
             "gbps": round(alg / (us * 1e-6) / 1e9, 1)}
 
 
+def time_dcp(dsa, synth, wl, spec, dev, G=8, reps=10):
+    """The DCP shard layout on one GPU: the batch as G round-robin KV shards.
+    Times one rank's share at its real shape (its indexer + top-k over L/G
+    positions, its partial over its share of the rows), the merge, the LSE
+    combine, and the whole G-shard step run on this one GPU."""
+    shards = synth.shard_round_robin(wl, G)
+    views = [(dsa.Pool(sh.pool, sh.num_pages, spec.kv_dtype), sh.page_table, sh.tok_pos,
+              sh.max_ctx) for sh in shards]
+    path = dsa.DcpPath(views, wl.q_offsets, wl.max_q, spec.k, kv_tile=64, sm_scale=spec.sm_scale)
+    stream = torch.cuda.current_stream(dev)
+    path.step(wl.q_idx, wl.w, wl.q)
+    torch.cuda.synchronize()
+    calls = {"rank0_select": lambda: path.local_select(0, wl.q_idx, wl.w),
+             "merge": path.merge,
+             "rank0_attend": lambda: path.local_attend(0, wl.q),
+             "combine": lambda: dsa.combine_shards(path.o_part, path.lse_part, path.out, path.lse),
+             "all_shards_step": lambda: path.step(wl.q_idx, wl.w, wl.q)}
+    res = {}
+    for name, fn in calls.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) * 1000.0 / reps, 2)
+    for v in views:
+        v[0].close()
+    return {"shards": G, **res,
+            "note": "one GPU holds all shards; a rank's share is rank0_select + rank0_attend, "
+                    "the exchanges (all-gather of local top-k, reduce of partials) are not run"}
+
+
 def flops(spec):
     T, k = spec.num_tokens, spec.k
     vis = sum(min(L, p + 1) for L, q in zip(spec.ctx_lens, spec.q_per_req)
@@ -141,6 +174,7 @@ def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
 # selection (index_topk) is five launches: sample pass, threshold, emit pass,
 # select, fallback.
 KERNEL_PATTERNS = [
+    ("dcp_merge", r"dcp_merge_kernel"),
     ("index_scores", r"index_kernel(ILi0E|<0>)"), ("index_sample", r"index_kernel(ILi1E|<1>)"),
     ("index_emit", r"index_kernel(ILi2E|<2>)"), ("threshold", r"threshold_kernel"),
     ("select", r"select_kernel"), ("fallback", r"fallback_kernel"), ("topk", r"topk_kernel"),
@@ -148,7 +182,8 @@ KERNEL_PATTERNS = [
 FUSED_SELECT = ("index_sample", "threshold", "index_emit", "select", "fallback")
 KERNEL_SOURCES = {"index_scores": ("dsa_index.hip",), "topk": ("dsa_topk.hip",),
                   "index_topk": ("dsa_index.hip", "dsa_topk.hip"),
-                  "partial": ("dsa_partial.hip",), "combine": ("dsa_partial.hip",)}
+                  "partial": ("dsa_partial.hip",), "combine": ("dsa_partial.hip",),
+                  "dcp_merge": ("dsa_topk.hip",)}
 for _k in FUSED_SELECT:
     KERNEL_SOURCES[_k] = KERNEL_SOURCES["index_topk"]
 CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
@@ -276,6 +311,7 @@ def main():
                     help="top-k selection: fused indexer + top-k (auto: rows up to 65,536) "
                          "or the score matrix + top-k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dcp", action="store_true", help="skip the DCP shard-layout timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
                          "(reference dispatch for HBM byte counters)")
@@ -412,6 +448,9 @@ def main():
         result["fused_select"] = {"fallback_tokens": fallback_tokens, "cap": path.cap,
                                   "unfused_us": unfused}
     result["kv_append"] = time_kv_append(dsa, spec.kv_dtype, dev)
+    if not args.no_dcp and spec.num_tokens * spec.k <= (1 << 22):
+        print("[bench] DCP shard layout", file=sys.stderr, flush=True)
+        result["dcp"] = time_dcp(dsa, synth, wl, spec, dev)
     if args.calibrate_copy:
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)

@@ -147,7 +147,7 @@ int32_t dsa_pool_kv_dtype(const dsa_pool* pool);
  *   processed).
  * ------------------------------------------------------------------------ */
 
-/* Indexer scores [LMSYS-1; VLLM: "the indexer is not partitioned"]:
+/* Indexer scores [LMSYS-1; VLLM: the indexer stays whole across GPUs]:
  *   scores[t*ld + p] = sum_{h<16} w[t*16+h] * max(0, q_idx[t,h,:] . key(p))
  * for p in [0, min(tok_pos[t], max_ctx-1)]; entries past that are not written.
  * q_idx: bf16 [num_tokens,16,128]; w: fp32 [num_tokens,16]; key(p) is the
@@ -261,6 +261,31 @@ dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_table, int32
  * lse: fp32 [num_tokens,64]. */
 dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,
                        int32_t num_splits, uint16_t* out, float* lse, void* stream);
+
+/* DCP shard layout on one GPU [VLLM Interpretation: the KV cache sharded
+ * round-robin by token, each of G ranks holding every G-th position].
+ * Shard r holds positions p = j*G + r at local position j; each shard runs
+ * dsa_index_scores + dsa_topk on its local positions (local tok_pos
+ * floor((tok_pos - r) / G), -1 when tok_pos < r).
+ *
+ * dsa_dcp_merge: the global top-k from the shards' local top-k lists, exactly
+ * what dsa_topk gives over the whole row (same tie rule and order): the union
+ * of the local lists contains it.  Inputs: local_idx [G][T][k] int32 (each
+ * shard's dsa_topk output: ascending local positions, -1 padded),
+ * local_scores [G][T][ld] fp32 (each shard's dsa_index_scores output).
+ * Outputs: idx [T][k] (global positions ascending, -1 padded) and, unless
+ * shard_idx is NULL, shard_idx [G][T][k]: the local positions of each
+ * shard's selected rows, ascending, -1 padded - the index each shard's
+ * dsa_sparse_mla_partial reads.  Limits: 1 <= G <= 16, G*k <= 16384.
+ *
+ * dsa_combine_shards: dsa_combine over shard-major partials, o_part
+ * [G][T][64][512] and lse_part [G][T][64] (shard r's single-split
+ * dsa_sparse_mla_partial writes the [T] slab r). */
+dsa_status dsa_dcp_merge(int32_t num_shards, int32_t num_tokens, int32_t k,
+                         const int32_t* local_idx, const float* local_scores, int64_t ld,
+                         int32_t* idx, int32_t* shard_idx, void* stream);
+dsa_status dsa_combine_shards(const float* o_part, const float* lse_part, int32_t num_tokens,
+                              int32_t num_shards, uint16_t* out, float* lse, void* stream);
 
 /* Writing new tokens into the cache [SGL "Size both memory pools": the paged
  * KV pool, FP8 by default on MI355X, and the separate DSA indexer pool].  Row i of the batch goes to

@@ -204,6 +204,22 @@ def topk_positions(scores: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def dcp_merge(shard_lists, k: int) -> np.ndarray:
+    """Global selection from round-robin KV shards ("A million-token context on
+    16 H200s", Interpretation: the cache is sharded by token, each of G ranks
+    holding every G-th position).  shard_lists[r] = (global positions, scores)
+    of shard r's own top-k; the result is the k best of their union under the
+    same rule as topk_positions (score desc, position asc), ascending, padded
+    with -1 to length k."""
+    pos = np.concatenate([np.asarray(p, dtype=np.int64) for p, _ in shard_lists])
+    sc = np.concatenate([np.asarray(v, dtype=np.float64) for _, v in shard_lists])
+    order = np.lexsort((pos, -sc))
+    keep = np.sort(pos[order[:min(k, pos.size)]])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:keep.size] = keep
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Step 3: attention over the selected rows, split-KV partials and combine
 # ---------------------------------------------------------------------------

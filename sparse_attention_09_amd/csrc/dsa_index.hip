@@ -37,7 +37,7 @@ constexpr int kRowBf16 = DSA_IDX_DIM;
 constexpr int kCandLds = dsa::kIndexMaxCap;   // emit pass: candidate slots per token (LDS)
 constexpr int kPageKeysBf16 = DSA_PAGE_TOKENS * DSA_IDX_DIM;
 constexpr int kSampleStride = dsa::kIndexSampleStride;
-constexpr int kSampleChunkPages = 2;   // sample pass: sampled pages per workgroup
+constexpr int kSampleChunkPages = 8;   // sample pass: sampled pages per workgroup
 
 enum Mode { kScores = 0, kSample = 1, kEmit = 2 };
 

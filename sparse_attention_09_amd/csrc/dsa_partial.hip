@@ -248,10 +248,13 @@ struct Stage<DSA_KV_BF16, NR, NT> {
 
 // Physical rows (page*64 + slot, or -1 when masked) of index columns
 // [cc, cc + kRowChunk) of token t, written to rows[]; with a bias array, also
-// 0 for a valid row and -inf for a masked one.
+// 0 for a valid row and -inf for a masked one.  *last (reset to -1 by the
+// caller) receives the largest chunk-relative column with a valid row.
+// nthreads must divide kRowChunk.
 __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int req, int pos, int cc,
                                              int cend, int32_t* rows, int tid, int nthreads,
-                                             float* bias = nullptr) {
+                                             int* last, float* bias = nullptr) {
+  const int lane = tid & 63;
   for (int i = tid; i < kRowChunk; i += nthreads) {
     const int col = cc + i;
     int phys = -1;
@@ -268,6 +271,8 @@ __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int re
     }
     rows[i] = phys;
     if (bias) bias[i] = phys >= 0 ? 0.f : kNegInf;
+    const uint64_t m = __ballot(phys >= 0);
+    if (m != 0ull && lane == 0) atomicMax(last, i + 63 - __clzll((long long)m));
   }
 }
 
@@ -393,6 +398,7 @@ constexpr int kTile4 = 128;
 struct Smem4 {
   uint16_t k[kTile4 * kKStride];
   int32_t rows[kRowChunk];
+  int last;                                     // last valid column of the row chunk
 };
 
 // Rows of a 128-row tile prefetched into registers while the previous tile is
@@ -436,10 +442,14 @@ __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
   Stage<KV, (kPR < TILE ? TILE - kPR : 32), kThreads4> st2;  // tail rows (BF16 only)
   for (int cc = c0; cc < c1; cc += kRowChunk) {
     const int cend = min(c1, cc + kRowChunk);
+    if (tid == 0) sm.last = -1;
     __syncthreads();
-    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads4);
+    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads4, &sm.last);
     __syncthreads();
-    const int ntile = (cend - cc + TILE - 1) / TILE;
+    // tiles up to the last valid row (trailing -1 padding is skipped: its rows
+    // would contribute exactly nothing)
+    const int ntile = (sm.last + TILE) / TILE;
+    if (ntile == 0) continue;
     st.load(a.latent, sm.rows, tid);
     st.store(sm.k, 0, tid);
     if constexpr (kPR < TILE) {
@@ -520,6 +530,7 @@ struct SmemV2 {
   f32x4 xs[8][TILE / 32][64];                   // partial S^T sent to the dh partner
   uint16_t p[DSA_HEADS * kPStride];             // P[head][row in PV operand order]
   float red[2][2][2][16];                       // [rh][hp][dh][head]: max / l partials
+  int last;                                     // last valid column of the row chunk
 };
 
 template <int KV, int TILE, bool kFinal>
@@ -686,10 +697,14 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
     }
     for (int cc = c0; cc < c1; cc += kRowChunk) {
       const int cend = min(c1, cc + kRowChunk);
+      if (tid == 0) sm.last = -1;
       __syncthreads();
-      resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, sm.bias);
+      resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
       __syncthreads();
-      const int ntile = (cend - cc + TILE - 1) / TILE;
+      // tiles up to the last valid row (trailing -1 padding is skipped: its
+      // rows would contribute exactly nothing)
+      const int ntile = (sm.last + TILE) / TILE;
+      if (ntile == 0) continue;
       st.load(a.latent, sm.rows, tid);
       st.store(sm.k[0], 0, tid);
       if constexpr (SmemV2<TILE>::kNBuf == 2) {
@@ -758,26 +773,29 @@ hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Combine: one thread per (token, head, 8 columns).
+// Part s of token t sits at slot t*ts + s*ss (token-major splits: ts = S,
+// ss = 1; shard-major parts: ts = 1, ss = T).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int T,
-                                                      int S, uint16_t* __restrict__ out,
+                                                      int S, int64_t ts, int64_t ss,
+                                                      uint16_t* __restrict__ out,
                                                       float* __restrict__ lse_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // token*64 + head
   if (row >= T * DSA_HEADS) return;
   const int lane = threadIdx.x & 63;
   const int t = row / DSA_HEADS, h = row % DSA_HEADS;
   float m = kNegInf;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_part[(int64_t(t) * S + s) * DSA_HEADS + h]);
+  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_part[(t * ts + s * ss) * DSA_HEADS + h]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != kNegInf) {
     for (int s = 0; s < S; ++s) {
-      const float ls = lse_part[(int64_t(t) * S + s) * DSA_HEADS + h];
+      const float ls = lse_part[(t * ts + s * ss) * DSA_HEADS + h];
       if (ls == kNegInf) continue;
       const float wgt = expf(ls - m);
       tot += wgt;
       const float4* src = reinterpret_cast<const float4*>(
-          o_part + ((int64_t(t) * S + s) * DSA_HEADS + h) * DSA_D_LATENT + 8 * lane);
+          o_part + ((t * ts + s * ss) * DSA_HEADS + h) * DSA_D_LATENT + 8 * lane);
       const float4 x0 = src[0], x1 = src[1];
       acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
       acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
@@ -890,24 +908,40 @@ extern "C" dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_t
                      stream);
 }
 
-extern "C" dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,
-                                  int32_t num_splits, uint16_t* out, float* lse, void* stream) {
-  if (num_tokens < 0) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_combine: num_tokens < 0");
-  if (num_splits < 1) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_combine: num_splits must be >= 1");
+static dsa_status run_combine(const char* who, const float* o_part, const float* lse_part,
+                              int32_t num_tokens, int32_t parts, bool shard_major, uint16_t* out,
+                              float* lse, void* stream) {
+  const std::string w(who);
+  if (num_tokens < 0) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": num_tokens < 0");
+  if (parts < 1) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": the part count must be >= 1");
   if (num_tokens == 0) return dsa::ok();
   if (!o_part || !lse_part || !out || !lse)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_combine: pointers must be non-null");
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": pointers must be non-null");
   if (!dsa::aligned(o_part, 16) || !dsa::aligned(out, 16) || !dsa::aligned(lse_part, 4) ||
       !dsa::aligned(lse, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_combine: o_part and out must be 16-byte aligned");
+    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": o_part and out must be 16-byte aligned");
   const int64_t rows = int64_t(num_tokens) * DSA_HEADS;
   if ((rows + 3) / 4 > 0x7fffffff)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_combine: too many tokens for one launch");
+    return dsa::fail(DSA_ERR_UNSUPPORTED, w + ": too many tokens for one launch");
+  const int64_t ts = shard_major ? 1 : parts, ss = shard_major ? num_tokens : 1;
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), o_part, lse_part, num_tokens, num_splits,
+                     static_cast<hipStream_t>(stream), o_part, lse_part, num_tokens, parts, ts, ss,
                      out, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
-    return dsa::fail(DSA_ERR_HIP, std::string("dsa_combine: launch failed: ") + hipGetErrorString(e));
+    return dsa::fail(DSA_ERR_HIP, w + ": launch failed: " + hipGetErrorString(e));
   return dsa::ok();
+}
+
+extern "C" dsa_status dsa_combine(const float* o_part, const float* lse_part, int32_t num_tokens,
+                                  int32_t num_splits, uint16_t* out, float* lse, void* stream) {
+  return run_combine("dsa_combine", o_part, lse_part, num_tokens, num_splits, false, out, lse,
+                     stream);
+}
+
+extern "C" dsa_status dsa_combine_shards(const float* o_part, const float* lse_part,
+                                         int32_t num_tokens, int32_t num_shards, uint16_t* out,
+                                         float* lse, void* stream) {
+  return run_combine("dsa_combine_shards", o_part, lse_part, num_tokens, num_shards, true, out, lse,
+                     stream);
 }

@@ -447,11 +447,15 @@ constexpr int kSelMax = 6144;         // candidates one selection workgroup hold
 constexpr int kMaxChunks = kSeg / dsa::kIndexChunk;
 constexpr int kRankSlack = 8;         // extra sample rank: fewer short-of-k rows
 
-struct Sel {
+// Block-level helpers for an NT-thread workgroup (NT a multiple of 64, at
+// least 256).
+template <int NT>
+struct SelT {
   uint32_t hist[2][256];
-  uint32_t wtmp[4][4];
+  uint32_t wtmp[NT / 64][4];
   uint32_t digit, above;
 };
+using Sel = SelT<kSmallThreads>;
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
@@ -464,15 +468,16 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
-// Exclusive scan over a 256-thread workgroup; *total gets the sum.  Barriers.
-__device__ __forceinline__ uint32_t scan256(uint32_t v, Sel& s, uint32_t* total) {
+// Exclusive scan over the workgroup; *total gets the sum.  Barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t scan_block(uint32_t v, SelT<NT>& s, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v, lane);
   if (lane == 63) s.wtmp[wave][0] = inc;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const uint32_t x = s.wtmp[i][0];
     before += i < wave ? x : 0u;
     tot += x;
@@ -481,11 +486,15 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, Sel& s, uint32_t* total)
   *total = tot;
   return before + inc - v;
 }
+__device__ __forceinline__ uint32_t scan256(uint32_t v, Sel& s, uint32_t* total) {
+  return scan_block<kSmallThreads>(v, s, total);
+}
 
-// Minimum and maximum of keys (lo/hi per thread) and a count sum over a
-// 256-thread workgroup.  Barriers.
-__device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint32_t n,
-                                          uint32_t* glo, uint32_t* ghi, uint32_t* gn) {
+// Minimum and maximum of keys (lo/hi per thread) and a count sum over the
+// workgroup.  Barriers.
+template <int NT>
+__device__ __forceinline__ void minmax_block(SelT<NT>& s, uint32_t lo, uint32_t hi, uint32_t n,
+                                             uint32_t* glo, uint32_t* ghi, uint32_t* gn) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   lo = wave_min(lo);
   hi = wave_max(hi);
@@ -500,7 +509,7 @@ __device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint
   hi = s.wtmp[0][2];
   n = s.wtmp[0][3];
 #pragma unroll
-  for (int i = 1; i < 4; ++i) {
+  for (int i = 1; i < NT / 64; ++i) {
     lo = min(lo, s.wtmp[i][1]);
     hi = max(hi, s.wtmp[i][2]);
     n += s.wtmp[i][3];
@@ -510,16 +519,20 @@ __device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint
   *ghi = hi;
   *gn = n;
 }
+__device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint32_t n,
+                                          uint32_t* glo, uint32_t* ghi, uint32_t* gn) {
+  minmax_block<kSmallThreads>(s, lo, hi, n, glo, ghi, gn);
+}
 
-// k-th largest of a key multiset spread over a 256-thread workgroup
-// (1 <= k <= its size; every key in [kmin, kmax]).  Radix selection on
-// d = key - kmin, 8-bit digits from the top bit of kmax - kmin down, so the
-// first digit already spreads the keys.  `each(f)` calls f on every key the
-// calling thread holds.  Returns the key; *r_out gets how many keys equal to
-// it belong to the k largest.  Barriers.
-template <class Each>
-__device__ __forceinline__ uint32_t radix_select256(Sel& s, uint32_t k_rem, uint32_t kmin,
-                                                    uint32_t kmax, Each each, uint32_t* r_out) {
+// k-th largest of a key multiset spread over the workgroup (1 <= k <= its
+// size; every key in [kmin, kmax]).  Radix selection on d = key - kmin, 8-bit
+// digits from the top bit of kmax - kmin down, so the first digit already
+// spreads the keys.  `each(f)` calls f on every key the calling thread holds.
+// Returns the key; *r_out gets how many keys equal to it belong to the k
+// largest.  Barriers.
+template <int NT, class Each>
+__device__ __forceinline__ uint32_t radix_select_block(SelT<NT>& s, uint32_t k_rem, uint32_t kmin,
+                                                       uint32_t kmax, Each each, uint32_t* r_out) {
   const int tid = threadIdx.x;
   const uint32_t span = kmax - kmin;
   if (span == 0) {
@@ -528,12 +541,12 @@ __device__ __forceinline__ uint32_t radix_select256(Sel& s, uint32_t k_rem, uint
   }
   const int passes = (32 - __clz(span) + 7) / 8;
   uint32_t prefix = 0;   // decided high digits of d
-  s.hist[0][tid] = 0;
+  if (tid < 256) s.hist[0][tid] = 0;
   __syncthreads();
   for (int pass = 0; pass < passes; ++pass) {
     const int sh = 8 * (passes - 1 - pass);
     uint32_t* h = s.hist[pass & 1];
-    s.hist[(pass + 1) & 1][tid] = 0;   // the next pass's histogram
+    if (tid < 256) s.hist[(pass + 1) & 1][tid] = 0;   // the next pass's histogram
     each([&](uint32_t key) {
       const uint32_t d = (key - kmin) >> sh;
       if ((d >> 8) == prefix) atomicAdd(&h[d & 255u], 1u);
@@ -566,6 +579,11 @@ __device__ __forceinline__ uint32_t radix_select256(Sel& s, uint32_t k_rem, uint
   }
   *r_out = k_rem;
   return kmin + prefix;
+}
+template <class Each>
+__device__ __forceinline__ uint32_t radix_select256(Sel& s, uint32_t k_rem, uint32_t kmin,
+                                                    uint32_t kmax, Each each, uint32_t* r_out) {
+  return radix_select_block<kSmallThreads>(s, k_rem, kmin, kmax, each, r_out);
 }
 
 // One workgroup per token.  Sample column q lies at position
@@ -733,6 +751,150 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
   }
 }
 
+// ================================================================ DCP merge
+// Round-robin KV shards (position p lives on shard p % G at local position
+// p / G): each shard selects its local top-k; the global top-k is contained in
+// the union of those lists (a position outside its shard's list is beaten by k
+// positions of that shard already), so one exact selection over at most G*k
+// candidates under the same rule gives it.  One 1024-thread workgroup per token.
+constexpr int kMergeMax = 16384;      // G*k candidates held in LDS
+constexpr int kMaxShards = 16;
+
+constexpr int kMergeThreads = 1024;
+using MSel = SelT<kMergeThreads>;
+
+struct MergeSmem {
+  uint32_t key[kMergeMax];    // candidate keys; after the selection, the kept positions
+  int32_t pos[kMergeMax];     // global positions (-1: empty slot)
+  MSel s;
+};
+
+__global__ __launch_bounds__(kMergeThreads) void dcp_merge_kernel(
+    int G, int T, int k, const int32_t* __restrict__ local_idx, const float* __restrict__ local_scores,
+    int64_t ld, int32_t* __restrict__ idx_out, int32_t* __restrict__ shard_idx) {
+  __shared__ MergeSmem sm;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int n = G * k;
+  // ---- load: candidate e = r*k + i is entry i of shard r's list
+  uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
+  for (int base = 0; base < n; base += kMergeThreads * 8) {
+    int32_t j[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + tid;
+      j[u] = -1;
+      if (e < n) j[u] = local_idx[(int64_t(e / k) * T + t) * k + e % k];
+    }
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + tid;
+      const int r = e < n ? e / k : 0;
+      v[u] = local_scores[(int64_t(r) * T + t) * ld + (j[u] >= 0 ? j[u] : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + tid;
+      if (e < n) {
+        const bool ok = j[u] >= 0;
+        const uint32_t key = ok ? dsa::float_key(v[u]) : 0u;
+        sm.key[e] = key;
+        sm.pos[e] = ok ? j[u] * G + e / k : -1;
+        nv += ok ? 1u : 0u;
+        lo = ok ? min(lo, key) : lo;
+        hi = ok ? max(hi, key) : hi;
+      }
+    }
+  }
+  uint32_t kmin, kmax, N;
+  minmax_block<kMergeThreads>(sm.s, lo, hi, nv, &kmin, &kmax, &N);   // barriers publish sm.key / sm.pos
+  // ---- the kept set: everything when at most k, else key > tau plus the r
+  // lowest positions among key == tau
+  uint32_t tau = 0, r_eq = 0, p_cut = 0x7FFFFFFFu;
+  bool all = N <= uint32_t(k);
+  if (!all) {
+    tau = radix_select_block<kMergeThreads>(
+        sm.s, uint32_t(k), kmin, kmax,
+        [&](auto&& f) {
+          for (int e = tid; e < n; e += kMergeThreads)
+            if (sm.pos[e] >= 0) f(sm.key[e]);
+        },
+        &r_eq);
+    uint32_t ne = 0;
+    for (int e = tid; e < n; e += kMergeThreads) ne += (sm.pos[e] >= 0 && sm.key[e] == tau) ? 1u : 0u;
+    uint32_t n_eq, d0, d1;
+    minmax_block<kMergeThreads>(sm.s, 0u, 0u, ne, &d0, &d1, &n_eq);
+    if (r_eq < n_eq) {
+      // the r_eq-th smallest position among the ties = r_eq-th largest of ~pos
+      uint32_t rr;
+      const uint32_t inv = radix_select_block<kMergeThreads>(
+          sm.s, r_eq, 0x80000000u, 0xFFFFFFFFu,
+          [&](auto&& f) {
+            for (int e = tid; e < n; e += kMergeThreads)
+              if (sm.pos[e] >= 0 && sm.key[e] == tau) f(~uint32_t(sm.pos[e]));
+          },
+          &rr);
+      p_cut = ~inv;
+    }
+  }
+  // ---- drop the positions not kept (each thread its own entries), then
+  // compact the kept ones (any order) into the key array, free by then
+  uint32_t nk = 0;
+  for (int e = tid; e < n; e += kMergeThreads) {
+    const int32_t p = sm.pos[e];
+    const uint32_t key = sm.key[e];
+    const bool keep = p >= 0 && (all || key > tau || (key == tau && uint32_t(p) <= p_cut));
+    if (!keep && p >= 0) sm.pos[e] = -1;
+    nk += keep ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t w = scan_block<kMergeThreads>(nk, sm.s, &total);   // its barriers order the key reads before the writes
+  for (int e = tid; e < n; e += kMergeThreads) {
+    const int32_t p = sm.pos[e];
+    if (p >= 0) sm.key[w++] = uint32_t(p);
+  }
+  // ---- bitonic sort of the kept positions (padded to a power of two)
+  const int m = int(total);
+  int P = 1;
+  while (P < m) P <<= 1;
+  for (int e = m + tid; e < P; e += kMergeThreads) sm.key[e] = 0x7FFFFFFFu;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int e = tid; e < P / 2; e += kMergeThreads) {
+        const int a = 2 * e - (e & (stride - 1));   // lower index of the pair
+        const int b = a + stride;
+        const bool up = (a & size) == 0;
+        const uint32_t x = sm.key[a], y = sm.key[b];
+        if ((x > y) == up) {
+          sm.key[a] = y;
+          sm.key[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // ---- global list, then each shard's local list (ascending, -1 padded)
+  int32_t* out = idx_out + int64_t(t) * k;
+  for (int i = tid; i < k; i += kMergeThreads) out[i] = i < m ? int32_t(sm.key[i]) : -1;
+  if (shard_idx) {
+    const int E = (m + kMergeThreads - 1) / kMergeThreads;
+    const int q0 = min(tid * E, m), q1 = min(q0 + E, m);
+    for (int r = 0; r < G; ++r) {
+      uint32_t c = 0;
+      for (int q = q0; q < q1; ++q) c += (int(sm.key[q]) % G == r) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t o = scan_block<kMergeThreads>(c, sm.s, &tot);
+      int32_t* dst = shard_idx + (int64_t(r) * T + t) * k;
+      for (int q = q0; q < q1; ++q) {
+        const int p = int(sm.key[q]);
+        if (p % G == r) dst[o++] = p / G;
+      }
+      for (int i = int(tot) + tid; i < k; i += kMergeThreads) dst[i] = -1;
+    }
+  }
+}
+
 // Persistent over the fallback list (every workgroup leaves once the list is
 // exhausted).
 __global__ __launch_bounds__(kThreads) void fallback_kernel(RowArgs a, IndexIn f,
@@ -891,5 +1053,29 @@ extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dsa::fail(DSA_ERR_HIP, std::string("dsa_index_topk: launch failed: ") + hipGetErrorString(e));
+  return dsa::ok();
+}
+
+extern "C" dsa_status dsa_dcp_merge(int32_t num_shards, int32_t num_tokens, int32_t k,
+                                    const int32_t* local_idx, const float* local_scores,
+                                    int64_t ld, int32_t* idx, int32_t* shard_idx, void* stream) {
+  if (num_shards < 1 || num_shards > kMaxShards)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need 1 <= num_shards <= 16");
+  if (num_tokens < 0 || k < 1)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need num_tokens >= 0 and k >= 1");
+  if (int64_t(num_shards) * k > kMergeMax)
+    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_dcp_merge: num_shards * k above 16384");
+  if (num_tokens == 0) return dsa::ok();
+  if (!local_idx || !local_scores || !idx)
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: local_idx, local_scores and idx must be non-null");
+  if (ld < 1 || !dsa::aligned(local_idx, 4) || !dsa::aligned(local_scores, 4) ||
+      !dsa::aligned(idx, 4) || (shard_idx && !dsa::aligned(shard_idx, 4)))
+    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need ld >= 1 and 4-byte aligned arrays");
+  hipLaunchKernelGGL(dcp_merge_kernel, dim3(num_tokens), dim3(kMergeThreads), 0,
+                     static_cast<hipStream_t>(stream), num_shards, num_tokens, k, local_idx,
+                     local_scores, ld, idx, shard_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string("dsa_dcp_merge: launch failed: ") + hipGetErrorString(e));
   return dsa::ok();
 }

@@ -39,7 +39,7 @@ EXPORTS = [
     "dsa_pool_num_pages", "dsa_pool_kv_dtype",
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
     "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
-    "dsa_index_topk_workspace_bytes", "dsa_index_topk",
+    "dsa_index_topk_workspace_bytes", "dsa_index_topk", "dsa_dcp_merge", "dsa_combine_shards",
 ]
 
 
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
             "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "dsa_kv_append": (i32, [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]),
             "dsa_index_topk_workspace_bytes": (sz, [i32, i32, i32]),
+            "dsa_dcp_merge": (i32, [i32, i32, i32, vp, vp, i64, vp, vp, vp]),
+            "dsa_combine_shards": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "dsa_index_topk": (i32, [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, i32, i32, i32,
                                      vp, vp, sz, vp]),
         }
@@ -363,6 +365,40 @@ def combine(o_part: torch.Tensor, lse_part: torch.Tensor, out=None, lse=None):
     return out, lse
 
 
+def dcp_merge(local_idx: torch.Tensor, local_scores: torch.Tensor, idx=None, shard_idx=None,
+              want_shard_idx: bool = True):
+    """Global top-k of round-robin KV shards from their local top-k lists.
+    local_idx [G, T, k] int32, local_scores [G, T, ld] fp32."""
+    dev = local_idx.device
+    G, T, k = local_idx.shape
+    _need(local_idx, "local_idx", torch.int32, dev)
+    _need(local_scores, "local_scores", torch.float32, dev)
+    if local_scores.dim() != 3 or local_scores.shape[0] != G or local_scores.shape[1] != T:
+        raise ValueError("local_scores must be [G, T, ld]")
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if shard_idx is None and want_shard_idx:
+        shard_idx = torch.empty((G, T, k), dtype=torch.int32, device=dev)
+    _check(lib().dsa_dcp_merge(G, T, k, _ptr(local_idx), _ptr(local_scores), local_scores.shape[2],
+                               _ptr(idx), _ptr(shard_idx), _stream(dev)))
+    return idx, shard_idx
+
+
+def combine_shards(o_part: torch.Tensor, lse_part: torch.Tensor, out=None, lse=None):
+    """LSE merge of shard-major partials o_part [G, T, 64, 512], lse_part [G, T, 64]."""
+    dev = o_part.device
+    G, T = o_part.shape[0], o_part.shape[1]
+    _need(o_part, "o_part", torch.float32, dev, (G, T, HEADS, D_LATENT))
+    _need(lse_part, "lse_part", torch.float32, dev, (G, T, HEADS))
+    if out is None:
+        out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    _check(lib().dsa_combine_shards(_ptr(o_part), _ptr(lse_part), T, G, _ptr(out), _ptr(lse),
+                                    _stream(dev)))
+    return out, lse
+
+
 def kv_append(pool: Pool, page_table, req, pos, latent, keys=None):
     """Quantize (FP8 pools) or copy (BF16 pools) new latent rows, with their
     indexer keys, into the pool at (request, position)."""
@@ -479,3 +515,68 @@ class DsaPath:
     def step(self, q_idx, w, q):
         self.select(q_idx, w)
         return self.attend(q)
+
+
+class DcpPath:
+    """One step over G round-robin KV shards held on one GPU, each shard as a
+    DCP rank would hold it (positions p = j*G + r at local position j, its own
+    pool and page table, local token positions floor((pos - r) / G)): per
+    shard dsa_index_scores + dsa_topk on local positions, dsa_dcp_merge for
+    the global top-k and each shard's share of it, per shard
+    dsa_sparse_mla_partial over that share, and dsa_combine_shards.  Buffers
+    are allocated once for a fixed batch shape.
+
+    shards: list of (pool, page_table, local_tok_pos, local_max_ctx)."""
+
+    def __init__(self, shards, q_offsets, max_q: int, k: int, kv_tile: int = 64,
+                 sm_scale: Optional[float] = None):
+        self.shards = list(shards)
+        self.G = len(self.shards)
+        if not 1 <= self.G <= 16:
+            raise ValueError("1 to 16 shards")
+        self.q_offsets, self.max_q, self.k = q_offsets, int(max_q), int(k)
+        self.kv_tile = int(kv_tile)
+        self.sm_scale = default_sm_scale() if sm_scale is None else float(sm_scale)
+        dev = self.shards[0][0].device
+        T = self.shards[0][2].numel()
+        self.T = T
+        lmax = max(int(m) for _, _, _, m in self.shards)
+        self.ld = (max(lmax, 1) + 3) // 4 * 4
+        G, k = self.G, self.k
+        self.scores = torch.empty((G, T, self.ld), dtype=torch.float32, device=dev)
+        self.local_idx = torch.empty((G, T, k), dtype=torch.int32, device=dev)
+        self.topk_ws = []
+        for _, _, _, m in self.shards:
+            need = topk_workspace_bytes(T, int(m), k)
+            self.topk_ws.append(torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.shard_idx = torch.empty((G, T, k), dtype=torch.int32, device=dev)
+        self.o_part = torch.empty((G, T, HEADS, D_LATENT), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((G, T, HEADS), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+
+    def local_select(self, r: int, q_idx, w):
+        """Shard r's own top-k over its local positions (what rank r computes)."""
+        pool, pt, tok_pos, m = self.shards[r]
+        index_scores(pool, pt, self.q_offsets, tok_pos, q_idx, w, self.max_q, int(m),
+                     self.scores[r], self.ld)
+        topk(self.scores[r], tok_pos, self.k, int(m), self.local_idx[r], self.topk_ws[r])
+
+    def merge(self):
+        return dcp_merge(self.local_idx, self.scores, self.idx, self.shard_idx)
+
+    def local_attend(self, r: int, q):
+        """Shard r's partial over its share of the selected rows."""
+        pool, pt, tok_pos, _ = self.shards[r]
+        sparse_mla_partial(pool, pt, self.q_offsets, tok_pos, q, self.shard_idx[r], self.sm_scale,
+                           self.kv_tile, 1, self.o_part[r].view(self.T, 1, HEADS, D_LATENT),
+                           self.lse_part[r].view(self.T, 1, HEADS))
+
+    def step(self, q_idx, w, q):
+        for r in range(self.G):
+            self.local_select(r, q_idx, w)
+        self.merge()
+        for r in range(self.G):
+            self.local_attend(r, q)
+        return combine_shards(self.o_part, self.lse_part, self.out, self.lse)

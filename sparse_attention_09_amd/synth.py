@@ -284,3 +284,46 @@ def random_index(s_tok_pos: torch.Tensor, width: int, seed: int, frac_invalid: f
     idx = torch.where((r >= frac_invalid / 2) & (r < frac_invalid),
                       tok_pos[:, None] + 1 + (u * 50).to(torch.int64), idx)
     return idx.to(torch.int32).to(device)
+
+
+def shard_round_robin(wl: Workload, G: int, seed: int = 77) -> list:
+    """The same batch as G round-robin KV shards (shard r holds positions
+    p = j*G + r at local position j, as in a DCP deployment), each a Workload
+    with its own pool and page table (a seeded permutation of its pages), the
+    tokens' local positions floor((pos - r) / G) (-1 when pos < r), and the
+    queries shared.  Pure data movement: rows are copied from `wl.pool`."""
+    s = wl.spec
+    dev = wl.pool.device
+    stride = ROW_STRIDE[s.kv_dtype]
+    n_rows = wl.num_pages * PAGE_TOKENS
+    lat = wl.pool[: n_rows * stride].view(n_rows, stride)
+    keys = wl.pool[n_rows * stride:].view(n_rows, KEY_ROW_BYTES)
+    pt = wl.page_table.to(torch.int64)
+    shards = []
+    for r in range(G):
+        lens = [max(0, -(-(L - r) // G)) for L in s.ctx_lens]
+        pages = [-(-n // PAGE_TOKENS) for n in lens]
+        npg = max(1, sum(pages))
+        perm = torch.randperm(npg, generator=_gen("cpu", seed, G, r)).to(dev)
+        local_pt = torch.zeros((s.num_reqs, max(1, max(pages) if pages else 1)), dtype=torch.int64,
+                               device=dev)
+        rows = torch.zeros(npg * PAGE_TOKENS, dtype=torch.int64, device=dev)
+        cur = 0
+        for b, (n, np_) in enumerate(zip(lens, pages)):
+            if np_ == 0:
+                continue
+            local_pt[b, :np_] = perm[cur:cur + np_]
+            cur += np_
+            j = torch.arange(n, device=dev)
+            p = j * G + r
+            src = pt[b, p // PAGE_TOKENS] * PAGE_TOKENS + p % PAGE_TOKENS
+            dst = local_pt[b, j // PAGE_TOKENS] * PAGE_TOKENS + j % PAGE_TOKENS
+            rows[dst] = src
+        pool = torch.cat([lat[rows].reshape(-1), keys[rows].reshape(-1)])
+        tok_pos = torch.div(wl.tok_pos.to(torch.int64) - r, G, rounding_mode="floor")
+        spec_r = dataclasses.replace(s, name=f"{s.name}_shard{r}of{G}", ctx_lens=lens,
+                                     shared_prefix=0, duplicate_prefix=False)
+        shards.append(Workload(spec_r, wl.seed, npg, pool, local_pt.to(torch.int32),
+                               wl.q_offsets, tok_pos.to(torch.int32), wl.tok_req, wl.q_idx, wl.w,
+                               wl.q))
+    return shards

@@ -226,6 +226,22 @@ def test_index_topk_validates_before_launch():
     L.dsa_pool_destroy(h)
 
 
+def test_dcp_calls_validate_before_launch():
+    L = dsa.lib()
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert L.dsa_dcp_merge(0, 4, 8, f, f, 64, f, f, None) == 1          # no shards
+    assert L.dsa_dcp_merge(17, 4, 8, f, f, 64, f, f, None) == 1         # too many
+    assert L.dsa_dcp_merge(8, 4, 4096, f, f, 4096, f, f, None) == 2     # G*k above 16384
+    assert L.dsa_dcp_merge(2, 4, 0, f, f, 64, f, f, None) == 1
+    assert L.dsa_dcp_merge(2, 4, 8, None, f, 64, f, f, None) == 1
+    assert L.dsa_dcp_merge(2, 4, 8, f, f, 0, f, f, None) == 1
+    assert L.dsa_dcp_merge(2, 0, 8, None, None, 64, None, None, None) == 0   # empty batch
+    assert L.dsa_combine_shards(f, f, 1, 0, f, f, None) == 1
+    assert L.dsa_combine_shards(None, f, 1, 2, f, f, None) == 1
+    assert L.dsa_combine_shards(None, None, 0, 2, None, None, None) == 0
+
+
 def test_compute_calls_validate_before_launch():
     L = dsa.lib()
     vp = ctypes.c_void_p

@@ -201,6 +201,41 @@ def test_topk_dominance_property():
     assert sel_keys[-1] < unsel_keys[0]
 
 
+def _shard_lists(scores, G, k):
+    """Each round-robin shard's own top-k (brute force on its positions)."""
+    out = []
+    for r in range(G):
+        gpos = list(range(r, len(scores), G))
+        best = sorted(gpos, key=lambda p: (-scores[p], p))[:k]
+        out.append((sorted(best), [scores[p] for p in sorted(best)]))
+    return out
+
+
+def test_dcp_merge_equals_full_row_selection():
+    # merging the shards' own top-k lists gives the whole row's top-k
+    rng = _rng(21)
+    for trial in range(300):
+        n = int(rng.integers(1, 90))
+        k = int(rng.integers(1, 40))
+        G = int(rng.choice([1, 2, 3, 5, 8, 13]))
+        scores = rng.integers(0, 5, size=n).astype(np.float32).tolist()    # heavy ties
+        got = O.dcp_merge(_shard_lists(scores, G, k), k).tolist()
+        assert got == _brute_topk(scores, k), (n, k, G)
+
+
+def test_dcp_merge_special_cases():
+    # equal scores everywhere: the k lowest positions, interleaved over shards
+    scores = [1.0] * 40
+    assert O.dcp_merge(_shard_lists(scores, 4, 6), 6).tolist() == [0, 1, 2, 3, 4, 5]
+    # more shards than positions: empty shards add nothing
+    assert O.dcp_merge(_shard_lists([2.0, 7.0], 8, 3), 3).tolist() == [0, 1, -1]
+    # one shard holding all of the winners
+    scores = [0.0] * 32
+    for p in range(3, 32, 4):
+        scores[p] = 5.0
+    assert O.dcp_merge(_shard_lists(scores, 4, 8), 8).tolist() == list(range(3, 32, 4))
+
+
 # --------------------------------------------------------------------------- attention
 def _rows(rng, m):
     return rng.standard_normal((m, 576))
