@@ -301,8 +301,8 @@ def main():
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="verify_fp8_64k")
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
@@ -312,6 +312,8 @@ def main():
                          "or the score matrix + top-k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dcp", action="store_true", help="skip the DCP shard-layout timing")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing a HIP graph replay of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
                          "(reference dispatch for HBM byte counters)")
@@ -358,6 +360,20 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_graph = None
+    if not args.no_graph:
+        # the same step recorded once on a HIP graph and replayed (no host
+        # launch per kernel); every buffer is preallocated
+        replay = path.capture(wl.q_idx, wl.w, wl.q)
+        for _ in range(max(1, args.warmup // 4)):
+            replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / args.steps
 
     # per-kernel timing on the same stream (separate loop, events between calls)
     if path.fused_topk:
@@ -438,7 +454,9 @@ def main():
                    "kv_tile": plan.tile, "splits": plan.splits,
                    "combine": "in partial (one split)" if path.fused else "separate kernel",
                    "selection": "fused indexer + top-k" if path.fused_topk
-                   else "score matrix + top-k"},
+                   else "score matrix + top-k",
+                   "launch": "eager calls on one stream"},
+        "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
         "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
                 "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
         "kernels": kernels,

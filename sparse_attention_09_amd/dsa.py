@@ -516,6 +516,24 @@ class DsaPath:
         self.select(q_idx, w)
         return self.attend(q)
 
+    def capture(self, q_idx, w, q):
+        """Record one step on a HIP graph (every buffer is preallocated and no
+        call allocates, synchronizes or memsets, so the step is capturable).
+        Returns a callable that replays it on the current stream; the inputs
+        are read from the same tensors at every replay."""
+        if not self.fused and self.o_part is None:
+            self._alloc_parts()
+        s = torch.cuda.Stream(self.pool.device)
+        s.wait_stream(torch.cuda.current_stream(self.pool.device))
+        with torch.cuda.stream(s):
+            self.step(q_idx, w, q)             # warm-up outside the capture
+        torch.cuda.current_stream(self.pool.device).wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(q_idx, w, q)
+        self._graph = g
+        return g.replay
+
 
 class DcpPath:
     """One step over G round-robin KV shards held on one GPU, each shard as a

@@ -132,3 +132,30 @@ def test_fused_equals_unfused_calls():
         assert np.array_equal(got, want)
     ref = _oracle_idx(wl)
     assert np.array_equal(want, ref)
+
+
+def test_graph_replay_equals_eager():
+    """The whole step recorded on a HIP graph: every replay, with eager work
+    of the program between replays, gives the eager step's bits."""
+    wl = _gen(synth.spec("tiny_fp8"), seed=9)
+    for select in ("auto", "scores"):
+        say(f"[case] graph replay select={select}")
+        pool = make_pool(wl)
+        path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx,
+                           wl.spec.k, kv_tile=64, num_splits=1, sm_scale=wl.spec.sm_scale,
+                           select=select)
+        out, lse = path.step(wl.q_idx, wl.w, wl.q)
+        torch.cuda.synchronize()
+        want = (out.clone(), lse.clone(), path.idx.clone())
+        replay = path.capture(wl.q_idx, wl.w, wl.q)
+        for i in range(4):
+            path.out.fill_(0)
+            path.idx.fill_(-7)
+            torch.cuda.synchronize()
+            replay()
+            torch.cuda.synchronize()
+            assert torch.equal(path.out, want[0]) and torch.equal(path.lse, want[1])
+            assert torch.equal(path.idx, want[2]), f"replay {i}"
+            # eager work between replays
+            dsa.index_scores(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q_idx, wl.w,
+                             wl.max_q, wl.max_ctx)
