@@ -764,100 +764,136 @@ constexpr int kMergeThreads = 1024;
 using MSel = SelT<kMergeThreads>;
 
 struct MergeSmem {
-  uint32_t key[kMergeMax];    // candidate keys; after the selection, the kept positions
-  int32_t pos[kMergeMax];     // global positions (-1: empty slot)
+  // pass A: candidate keys (0: empty slot); afterwards the kept positions:
+  // those above the threshold from 0, the ties after them, then sorted
+  uint32_t buf[kMergeMax];
   MSel s;
+  uint32_t n_gt, n_eq;
 };
+
+// Loads candidate e (entry e % k of shard e / k): its key (0 when empty) and
+// global position.  Loads are issued for 8 candidates at once.
+struct MergeIn {
+  int G, T, k, n;
+  const int32_t* local_idx;
+  const float* local_scores;
+  int64_t ld;
+};
+
+template <class F>
+__device__ __forceinline__ void merge_for_each(const MergeIn& in, int t, F f) {
+  for (int base = 0; base < in.n; base += kMergeThreads * 8) {
+    int32_t j[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + threadIdx.x;
+      j[u] = -1;
+      if (e < in.n) j[u] = in.local_idx[(int64_t(e / in.k) * in.T + t) * in.k + e % in.k];
+    }
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + threadIdx.x;
+      const int r = e < in.n ? e / in.k : 0;
+      v[u] = in.local_scores[(int64_t(r) * in.T + t) * in.ld + (j[u] >= 0 ? j[u] : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + kMergeThreads * u + threadIdx.x;
+      const bool ok = e < in.n && j[u] >= 0;
+      f(e, ok ? dsa::float_key(v[u]) : 0u, ok ? j[u] * in.G + e / in.k : -1);
+    }
+  }
+}
+
+// Appends `val` at list position base + (count so far) for the lanes with
+// `cond`, one LDS atomic per wave.
+__device__ __forceinline__ void wave_append(bool cond, uint32_t val, uint32_t* counter,
+                                            uint32_t base, uint32_t* list) {
+  const uint64_t m = __ballot(cond);
+  if (m == 0ull) return;
+  const int lane = threadIdx.x & 63;
+  uint32_t first = 0;
+  if (lane == 0) first = atomicAdd(counter, uint32_t(__popcll((long long)m)));
+  first = __shfl(first, 0);
+  if (cond) {
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+    list[base + first + below] = val;
+  }
+}
 
 __global__ __launch_bounds__(kMergeThreads) void dcp_merge_kernel(
     int G, int T, int k, const int32_t* __restrict__ local_idx, const float* __restrict__ local_scores,
     int64_t ld, int32_t* __restrict__ idx_out, int32_t* __restrict__ shard_idx) {
   __shared__ MergeSmem sm;
   const int t = blockIdx.x, tid = threadIdx.x;
-  const int n = G * k;
-  // ---- load: candidate e = r*k + i is entry i of shard r's list
+  const MergeIn in{G, T, k, G * k, local_idx, local_scores, ld};
+  // ---- pass A: keys into LDS, count / range, the threshold key
   uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
-  for (int base = 0; base < n; base += kMergeThreads * 8) {
-    int32_t j[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = base + kMergeThreads * u + tid;
-      j[u] = -1;
-      if (e < n) j[u] = local_idx[(int64_t(e / k) * T + t) * k + e % k];
+  merge_for_each(in, t, [&](int e, uint32_t key, int32_t) {
+    if (e < in.n) sm.buf[e] = key;
+    if (key != 0u) {
+      ++nv;
+      lo = min(lo, key);
+      hi = max(hi, key);
     }
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = base + kMergeThreads * u + tid;
-      const int r = e < n ? e / k : 0;
-      v[u] = local_scores[(int64_t(r) * T + t) * ld + (j[u] >= 0 ? j[u] : 0)];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = base + kMergeThreads * u + tid;
-      if (e < n) {
-        const bool ok = j[u] >= 0;
-        const uint32_t key = ok ? dsa::float_key(v[u]) : 0u;
-        sm.key[e] = key;
-        sm.pos[e] = ok ? j[u] * G + e / k : -1;
-        nv += ok ? 1u : 0u;
-        lo = ok ? min(lo, key) : lo;
-        hi = ok ? max(hi, key) : hi;
-      }
-    }
+  });
+  if (tid == 0) {
+    sm.n_gt = 0;
+    sm.n_eq = 0;
   }
   uint32_t kmin, kmax, N;
-  minmax_block<kMergeThreads>(sm.s, lo, hi, nv, &kmin, &kmax, &N);   // barriers publish sm.key / sm.pos
-  // ---- the kept set: everything when at most k, else key > tau plus the r
-  // lowest positions among key == tau
-  uint32_t tau = 0, r_eq = 0, p_cut = 0x7FFFFFFFu;
-  bool all = N <= uint32_t(k);
+  minmax_block<kMergeThreads>(sm.s, lo, hi, nv, &kmin, &kmax, &N);   // barriers publish buf
+  const bool all = N <= uint32_t(k);
+  uint32_t tau = 0, r_eq = 0;
   if (!all) {
     tau = radix_select_block<kMergeThreads>(
         sm.s, uint32_t(k), kmin, kmax,
         [&](auto&& f) {
-          for (int e = tid; e < n; e += kMergeThreads)
-            if (sm.pos[e] >= 0) f(sm.key[e]);
+          for (int e = tid; e < in.n; e += kMergeThreads)
+            if (sm.buf[e] != 0u) f(sm.buf[e]);
         },
         &r_eq);
-    uint32_t ne = 0;
-    for (int e = tid; e < n; e += kMergeThreads) ne += (sm.pos[e] >= 0 && sm.key[e] == tau) ? 1u : 0u;
-    uint32_t n_eq, d0, d1;
-    minmax_block<kMergeThreads>(sm.s, 0u, 0u, ne, &d0, &d1, &n_eq);
-    if (r_eq < n_eq) {
-      // the r_eq-th smallest position among the ties = r_eq-th largest of ~pos
-      uint32_t rr;
-      const uint32_t inv = radix_select_block<kMergeThreads>(
-          sm.s, r_eq, 0x80000000u, 0xFFFFFFFFu,
-          [&](auto&& f) {
-            for (int e = tid; e < n; e += kMergeThreads)
-              if (sm.pos[e] >= 0 && sm.key[e] == tau) f(~uint32_t(sm.pos[e]));
-          },
-          &rr);
-      p_cut = ~inv;
+  }
+  __syncthreads();   // buf is reused below
+  // ---- pass B: positions above the threshold from 0, the ties after them
+  const uint32_t eq_base = all ? 0u : uint32_t(k) - r_eq;
+  merge_for_each(in, t, [&](int, uint32_t key, int32_t p) {
+    const bool gt = key != 0u && (all || key > tau);
+    const bool eq = key != 0u && !all && key == tau;
+    wave_append(gt, uint32_t(p), &sm.n_gt, 0u, sm.buf);
+    wave_append(eq, uint32_t(p), &sm.n_eq, eq_base, sm.buf);
+  });
+  __syncthreads();
+  const uint32_t n_eq = sm.n_eq;
+  if (!all && n_eq > r_eq) {
+    // keep the r_eq lowest positions among the ties: the r_eq-th largest of ~pos
+    uint32_t rr;
+    const uint32_t inv = radix_select_block<kMergeThreads>(
+        sm.s, r_eq, 0x80000000u, 0xFFFFFFFFu,
+        [&](auto&& f) {
+          for (uint32_t e = tid; e < n_eq; e += kMergeThreads) f(~sm.buf[eq_base + e]);
+        },
+        &rr);
+    const uint32_t p_cut = ~inv;
+    // compact the kept ties to the front of their region (each thread first
+    // reads its entries, then the scan's barriers order the writes after)
+    uint32_t mine[kMergeMax / kMergeThreads];
+    uint32_t c = 0;
+    for (uint32_t e = tid, i = 0; e < n_eq; e += kMergeThreads, ++i) {
+      const uint32_t p = sm.buf[eq_base + e];
+      if (p <= p_cut) mine[c++] = p;
     }
-  }
-  // ---- drop the positions not kept (each thread its own entries), then
-  // compact the kept ones (any order) into the key array, free by then
-  uint32_t nk = 0;
-  for (int e = tid; e < n; e += kMergeThreads) {
-    const int32_t p = sm.pos[e];
-    const uint32_t key = sm.key[e];
-    const bool keep = p >= 0 && (all || key > tau || (key == tau && uint32_t(p) <= p_cut));
-    if (!keep && p >= 0) sm.pos[e] = -1;
-    nk += keep ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t w = scan_block<kMergeThreads>(nk, sm.s, &total);   // its barriers order the key reads before the writes
-  for (int e = tid; e < n; e += kMergeThreads) {
-    const int32_t p = sm.pos[e];
-    if (p >= 0) sm.key[w++] = uint32_t(p);
+    uint32_t tot;
+    const uint32_t o = scan_block<kMergeThreads>(c, sm.s, &tot);
+    for (uint32_t i = 0; i < c; ++i) sm.buf[eq_base + o + i] = mine[i];
   }
   // ---- bitonic sort of the kept positions (padded to a power of two)
-  const int m = int(total);
+  const int m = all ? int(N) : k;
   int P = 1;
   while (P < m) P <<= 1;
-  for (int e = m + tid; e < P; e += kMergeThreads) sm.key[e] = 0x7FFFFFFFu;
+  for (int e = m + tid; e < P; e += kMergeThreads) sm.buf[e] = 0x7FFFFFFFu;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -865,10 +901,10 @@ __global__ __launch_bounds__(kMergeThreads) void dcp_merge_kernel(
         const int a = 2 * e - (e & (stride - 1));   // lower index of the pair
         const int b = a + stride;
         const bool up = (a & size) == 0;
-        const uint32_t x = sm.key[a], y = sm.key[b];
+        const uint32_t x = sm.buf[a], y = sm.buf[b];
         if ((x > y) == up) {
-          sm.key[a] = y;
-          sm.key[b] = x;
+          sm.buf[a] = y;
+          sm.buf[b] = x;
         }
       }
       __syncthreads();
@@ -876,18 +912,18 @@ __global__ __launch_bounds__(kMergeThreads) void dcp_merge_kernel(
   }
   // ---- global list, then each shard's local list (ascending, -1 padded)
   int32_t* out = idx_out + int64_t(t) * k;
-  for (int i = tid; i < k; i += kMergeThreads) out[i] = i < m ? int32_t(sm.key[i]) : -1;
+  for (int i = tid; i < k; i += kMergeThreads) out[i] = i < m ? int32_t(sm.buf[i]) : -1;
   if (shard_idx) {
     const int E = (m + kMergeThreads - 1) / kMergeThreads;
     const int q0 = min(tid * E, m), q1 = min(q0 + E, m);
     for (int r = 0; r < G; ++r) {
       uint32_t c = 0;
-      for (int q = q0; q < q1; ++q) c += (int(sm.key[q]) % G == r) ? 1u : 0u;
+      for (int q = q0; q < q1; ++q) c += (int(sm.buf[q]) % G == r) ? 1u : 0u;
       uint32_t tot;
       uint32_t o = scan_block<kMergeThreads>(c, sm.s, &tot);
       int32_t* dst = shard_idx + (int64_t(r) * T + t) * k;
       for (int q = q0; q < q1; ++q) {
-        const int p = int(sm.key[q]);
+        const int p = int(sm.buf[q]);
         if (p % G == r) dst[o++] = p / G;
       }
       for (int i = int(tot) + tid; i < k; i += kMergeThreads) dst[i] = -1;

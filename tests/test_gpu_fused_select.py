@@ -159,3 +159,30 @@ def test_graph_replay_equals_eager():
             # eager work between replays
             dsa.index_scores(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q_idx, wl.w,
                              wl.max_q, wl.max_ctx)
+
+
+@pytest.mark.parametrize("k", [1, 7, 3000, 5000])
+def test_fused_odd_k(k):
+    """k = 1, a small odd k, and k large enough that most rows exceed the
+    selection workgroup's candidate room and take the fallback."""
+    s = synth.Spec("odd_k_fp8", synth.KV_FP8, [9000, 4100, 130], [3, 2, 2], k)
+    wl = _gen(s, seed=11)
+    pool = make_pool(wl)
+    ref = _oracle_idx(wl)
+    for cap in (128, 16):
+        say(f"[case] fused k={k} cap={cap}")
+        got, _ = _fused(wl, pool, cap)
+        assert np.array_equal(got, ref)
+
+
+def test_fused_zero_context_bound():
+    """max_ctx = 0: nothing is visible, every index is -1 (as the unfused calls give)."""
+    wl = _gen(synth.spec("tiny_fp8"))
+    pool = make_pool(wl)
+    T, k = wl.num_tokens, wl.spec.k
+    ws = torch.empty(max(dsa.index_topk_workspace_bytes(T, 0, 128), 1), dtype=torch.uint8,
+                     device=DEV)
+    idx = dsa.index_topk(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q_idx, wl.w, wl.max_q,
+                         0, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((idx == -1).all())
