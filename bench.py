@@ -432,7 +432,7 @@ def main():
             d["tflops"] = round(fl[n] / (per_us[n] * 1e-6) / 1e12, 2)
         kernels[n] = d
     dom = max(names, key=lambda n: per_us[n])
-    path_bytes = sum(byts.values())
+    path_bytes = sum(byts[n] for n in names)     # the calls the step makes
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
     T = spec.num_tokens
     value = T / (ms_step * 1e-3)
