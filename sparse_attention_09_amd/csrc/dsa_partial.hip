@@ -32,6 +32,7 @@
 
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -72,6 +73,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 struct PartialArgs {
@@ -120,39 +131,71 @@ struct Stage;
 
 // FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.  Latent chunk
 // q (16 codes) is row q/32, columns 16(q%32)..+16, with the scale of group
-// (q%32)/4; rope chunk q is row q/4, rope columns 16(q%4)..+16.
+// (q%32)/4.  The rope (64 codes per row) is cut into NT equal pieces of
+// kRP = NR*64/NT bytes when that is 4 or 8 (tiles of 32 and 64 rows over 512
+// threads), so every thread stages the same number of latent chunks and one
+// rope piece and the staging has no per-thread branch; otherwise rope chunk q
+// (16 codes) is row q/4, rope columns 16(q%4)..+16.
 template <int NR, int NT>
 struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
   static constexpr int kStride = 640;
   static constexpr int kLC = (NR * 32 + NT - 1) / NT;
-  static constexpr int kRC = (NR * 4 + NT - 1) / NT;
+  static constexpr bool kLExact = kLC * NT == NR * 32;
+  static constexpr int kRP = (NR * 64) % NT == 0 ? NR * 64 / NT : 0;
+  static constexpr bool kRPiece = kRP == 4 || kRP == 8;
+  static constexpr int kRC = kRPiece ? 1 : (NR * 4 + NT - 1) / NT;
+  using RopeT = std::conditional_t<kRP == 4, uint32_t, std::conditional_t<kRP == 8, u32x2, u32x4>>;
   u32x4 lcode[kLC];
   float lscale[kLC];
-  u32x4 rcode[kRC];
+  RopeT rcode[kRC];
   float rscale[kRC];
   uint32_t lok, rok;   // bit i: chunk i holds a valid row
 
+  // Latent chunk i of this thread (row (tid + NT*i)/32) into registers.
+  __device__ __forceinline__ void load_latent(const uint8_t* latent, const int32_t* rows, int tid, int i) {
+    const int q = tid + NT * i;
+    const int phys = (kLExact || q < NR * 32) ? rows[q >> 5] : -1;
+    lok = (lok & ~(1u << i)) | (uint32_t(phys >= 0) << i);
+    const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
+    lcode[i] = *reinterpret_cast<const u32x4*>(row + 16 * (q & 31));
+    lscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
+  }
+  // This thread's rope piece (piece layout only).
+  __device__ __forceinline__ void load_rope_piece(const uint8_t* latent, const int32_t* rows, int tid) {
+    constexpr int kPerRow = 64 / kRP;
+    const int phys = rows[tid / kPerRow];
+    rok = uint32_t(phys >= 0);
+    const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
+    rcode[0] = *reinterpret_cast<const RopeT*>(row + DSA_D_LATENT + kRP * (tid % kPerRow));
+    rscale[0] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+  }
+
   // Unconditional loads: invalid rows read row 0 and are zeroed when stored.
   __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int tid) {
-    lok = rok = 0;
 #pragma unroll
-    for (int i = 0; i < kLC; ++i) {
-      const int q = tid + NT * i;
-      const int phys = q < NR * 32 ? rows[q >> 5] : -1;
-      lok |= uint32_t(phys >= 0) << i;
-      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
-      lcode[i] = *reinterpret_cast<const u32x4*>(row + 16 * (q & 31));
-      lscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
-    }
+    for (int i = 0; i < kLC; ++i) load_latent(latent, rows, tid, i);
+    if constexpr (kRPiece) {
+      load_rope_piece(latent, rows, tid);
+    } else {
+      rok = 0;
 #pragma unroll
-    for (int i = 0; i < kRC; ++i) {
-      const int q = tid + NT * i;
-      const int phys = q < NR * 4 ? rows[q >> 2] : -1;
-      rok |= uint32_t(phys >= 0) << i;
-      const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
-      rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (q & 3));
-      rscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+      for (int i = 0; i < kRC; ++i) {
+        const int q = tid + NT * i;
+        const int phys = q < NR * 4 ? rows[q >> 2] : -1;
+        rok |= uint32_t(phys >= 0) << i;
+        const uint8_t* row = latent + int64_t(max(phys, 0)) * kStride;
+        rcode[i] = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (q & 3));
+        rscale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+      }
     }
+  }
+
+  // 4 codes -> 4 bf16 (two dwords)
+  __device__ __forceinline__ static u32x2 dq4(uint32_t codes, float scale) {
+    float f[4];
+    dsa::fp8x4_to_f32(codes, f);
+    return u32x2{dsa::pack_bf16x2(f[0] * scale, f[1] * scale),
+                 dsa::pack_bf16x2(f[2] * scale, f[3] * scale)};
   }
 
   // 16 codes -> 16 bf16 = chunks `chunk` (even), `chunk`+1 of row r
@@ -161,15 +204,61 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
     uint32_t b[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      float f[4];
-      dsa::fp8x4_to_f32(codes[h], f);
-      b[2 * h] = dsa::pack_bf16x2(f[0] * scale, f[1] * scale);
-      b[2 * h + 1] = dsa::pack_bf16x2(f[2] * scale, f[3] * scale);
+      const u32x2 v = dq4(codes[h], scale);
+      b[2 * h] = v[0];
+      b[2 * h + 1] = v[1];
     }
     uint16_t* row = k + r * kKStride + 8 * chunk;
     const int sw = k_swz(r);
     *reinterpret_cast<u32x4*>(row + 8 * sw) = u32x4{b[0], b[1], b[2], b[3]};
     *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = u32x4{b[4], b[5], b[6], b[7]};
+  }
+
+  // piece p of row r: rope codes kRP*p..; bf16 chunk 64 + kRP*p/8, and
+  // within it 4*(p&1) values for 4-byte pieces
+  __device__ __forceinline__ void store_rope_piece(uint16_t* k, int r0, int tid) const {
+    constexpr int kPerRow = 64 / kRP;
+    const int r = r0 + tid / kPerRow, p = tid % kPerRow;
+    const bool ok = rok & 1u;
+    const float sc = ok ? rscale[0] : 0.f;
+    if constexpr (kRP == 4) {
+      const u32x2 v = dq4(ok ? rcode[0] : 0u, sc);
+      *reinterpret_cast<u32x2*>(k + k_chunk_off(r, DSA_D_LATENT / 8 + (p >> 1)) + 4 * (p & 1)) = v;
+    } else {
+      const u32x2 lo = dq4(ok ? rcode[0][0] : 0u, sc), hi = dq4(ok ? rcode[0][1] : 0u, sc);
+      *reinterpret_cast<u32x4*>(k + k_chunk_off(r, DSA_D_LATENT / 8 + p)) =
+          u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+
+  // The staging of one tile cut into kPieces small steps, to be spread
+  // between MFMAs: steps 0..2kLC-1 store half a latent chunk each (8 codes,
+  // one 16-byte LDS write), step 2kLC the rope piece, then one step per
+  // latent chunk load and one for the rope load.  Every store step runs
+  // before the first load step (a load reuses the registers a store reads).
+  static constexpr int kPieces = 3 * kLC + 2;
+  template <int J>
+  __device__ __forceinline__ void piece(uint16_t* k, int r0, const uint8_t* latent,
+                                        const int32_t* rows, int tid) {
+    static_assert(kRPiece && kLExact, "pieces need the uniform staging layout");
+    if constexpr (J < 2 * kLC) {
+      constexpr int i = J / 2, h = J % 2;
+      const int q = tid + NT * i;
+      const bool ok = (lok >> i) & 1u;
+      const float sc = ok ? lscale[i] : 0.f;
+      const u32x2 lo = dq4(ok ? lcode[i][2 * h] : 0u, sc);
+      const u32x2 hi = dq4(ok ? lcode[i][2 * h + 1] : 0u, sc);
+      const int r = r0 + (q >> 5);
+      // logical chunk 2(q%32) + h sits at physical chunk (2(q%32) + h) ^ swz(r)
+      *reinterpret_cast<u32x4*>(k + r * kKStride + 16 * (q & 31) + 8 * (h ^ k_swz(r))) =
+          u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else if constexpr (J == 2 * kLC) {
+      store_rope_piece(k, r0, tid);
+    } else if constexpr (J < 3 * kLC + 1) {
+      load_latent(latent, rows, tid, J - 2 * kLC - 1);
+    } else if constexpr (J == 3 * kLC + 1) {
+      load_rope_piece(latent, rows, tid);
+    }
   }
 
   // rows are stored at r0 + (tile row)
@@ -179,16 +268,20 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
     for (int i = 0; i < kLC; ++i) {
       const int q = tid + NT * i;
       const bool ok = (lok >> i) & 1u;
-      if (q < NR * 32)
+      if (kLExact || q < NR * 32)
         put16(k, r0 + (q >> 5), 2 * (q & 31), ok ? lcode[i] : z, ok ? lscale[i] : 0.f);
     }
+    if constexpr (kRPiece) {
+      store_rope_piece(k, r0, tid);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kRC; ++i) {
-      const int q = tid + NT * i;
-      const bool ok = (rok >> i) & 1u;
-      if (q < NR * 4)
-        put16(k, r0 + (q >> 2), DSA_D_LATENT / 8 + 2 * (q & 3), ok ? rcode[i] : z,
-              ok ? rscale[i] : 0.f);
+      for (int i = 0; i < kRC; ++i) {
+        const int q = tid + NT * i;
+        const bool ok = (rok >> i) & 1u;
+        if (q < NR * 4)
+          put16(k, r0 + (q >> 2), DSA_D_LATENT / 8 + 2 * (q & 3), ok ? rcode[i] : z,
+                ok ? rscale[i] : 0.f);
+      }
     }
   }
 };
@@ -579,7 +672,14 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   // P: written at head 32hp + 16dh + c, read as the A operand of head 32hp + 16hb + c
   uint16_t* pw = sm.p + (32 * hp + 16 * dh + c) * kPS;
 
-  auto compute_tile = [&](int it, const uint16_t* kt, auto&& after_qk) {
+  // stage(integral_constant<int, J>) is called after the QK MFMAs of k-step J
+  // (J = 0..kQS-1): work that needs no result of this tile, i.e. the next
+  // tile's staging with a double buffer.  For FP8 double buffering the steps
+  // are pinned between the MFMAs (a scheduling barrier after each k-step, the
+  // next K fragment read one step ahead), so the dequantization VALU work
+  // overlaps the matrix pipe instead of following it.
+  constexpr bool kPipeQK = SmemV2<TILE>::kNBuf == 2 && KV == DSA_KV_FP8_E4M3_S64 && kOMB == 1;
+  auto compute_tile = [&](int it, const uint16_t* kt, auto&& stage) {
     // S^T over this wave's rows and half of the dims, starting at the row bias
     f32x4 sacc[kOMB][2];
 #pragma unroll
@@ -590,22 +690,34 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       sacc[mb][1] = b;
     }
     const uint16_t* kq = kt + klane;
-#pragma unroll
-    for (int ks = 0; ks < kQS; ++ks) {
-      u32x4 kf[kOMB];
-#pragma unroll
-      for (int mb = 0; mb < kOMB; ++mb)
-        kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
-#pragma unroll
-      for (int mb = 0; mb < kOMB; ++mb)
+    if constexpr (kPipeQK) {
+      u32x4 kn = *reinterpret_cast<const u32x4*>(kq);
+      static_for<kQS>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        const u32x4 kf = kn;
+        if constexpr (ks + 1 < kQS) kn = *reinterpret_cast<const u32x4*>(kq + 32 * (ks + 1));
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
-                                           sacc[mb][hb]);
+          sacc[0][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[hb][ks]), sacc[0][hb]);
+        stage(KS);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kQS; ++ks) {
+        u32x4 kf[kOMB];
+#pragma unroll
+        for (int mb = 0; mb < kOMB; ++mb)
+          kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
+#pragma unroll
+        for (int mb = 0; mb < kOMB; ++mb)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
+                                             sacc[mb][hb]);
+      }
+      static_for<kQS>(stage);
     }
-    // work that needs no result of this tile (the next tile's staging with a
-    // double buffer) sits here, next to the MFMAs, for the scheduler to interleave
-    after_qk();
     // keep head block dh, send head block 1-dh to the partner (wave ^ 2)
     f32x4 sv[kOMB];
 #pragma unroll
@@ -715,9 +827,17 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
         st.load(a.latent, sm.rows + min(1, ntile - 1) * TILE, tid);
         __syncthreads();
         for (int it = 0; it < ntile; ++it) {
-          compute_tile(it, sm.k[it & 1], [&] {
-            st.store(sm.k[(it + 1) & 1], 0, tid);
-            st.load(a.latent, sm.rows + min(it + 2, ntile - 1) * TILE, tid);
+          uint16_t* knext = sm.k[(it + 1) & 1];
+          const int32_t* rows2 = sm.rows + min(it + 2, ntile - 1) * TILE;
+          compute_tile(it, sm.k[it & 1], [&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if constexpr (kPipeQK) {
+              static_assert(decltype(st)::kPieces <= kQS, "staging steps fit the k-steps");
+              st.template piece<j>(knext, 0, a.latent, rows2, tid);
+            } else if constexpr (j == kQS - 1) {
+              st.store(knext, 0, tid);
+              st.load(a.latent, rows2, tid);
+            }
           });
           __syncthreads();
         }
@@ -726,7 +846,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
         for (int it = 0; it < ntile; ++it) {
           const bool more = it + 1 < ntile;
           if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
-          compute_tile(it, sm.k[0], [] {});
+          compute_tile(it, sm.k[0], [](auto) {});
           __syncthreads();
           if (more) {
             st.store(sm.k[0], 0, tid);
