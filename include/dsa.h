@@ -203,9 +203,12 @@ dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table, int32
                           size_t workspace_bytes, void* stream);
 
 /* Dispatch plan of the Partial step [LMSYS-3 and Figure 4].  Host-only.
- *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose.
+ *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose
+ *   (64, or 32 when width < 1024).
  *   num_splits: KV splits per token, or 0 = choose from query parallelism
- *   (num_tokens) and cu_count (0 = 256, MI355X).
+ *   (num_tokens) and cu_count (0 = 256, MI355X): 1 when num_tokens >=
+ *   cu_count, else about one workgroup per CU with at least two tiles per
+ *   split: min(ceil(cu_count/num_tokens), iters_total/2), at least 1.
  * Output (host): tile, splits, iters_total = ceil(width/tile), iters_per_split
  * = ceil(iters_total/splits), cols_per_split = tile*iters_per_split,
  * virtual_cols = tile*iters_total, padding_cols = virtual_cols - width.

@@ -208,19 +208,22 @@ dsa_status dsa_plan_partial(int32_t num_tokens, int32_t width, int32_t kv_tile, 
   const int32_t cus = cu_count > 0 ? cu_count : kDefaultCUs;
   // Query parallelism: one workgroup per (token, split), one resident workgroup
   // per CU.  With at least a CU's worth of tokens a single split keeps every CU
-  // busy, and the larger tile cuts loop iterations, softmax updates and
-  // rescales; with few tokens, splits add the parallelism and smaller tiles
-  // keep the split boundaries fine-grained.
+  // busy.  With fewer, splits add workgroups up to one per CU, but each split
+  // keeps at least two tiles: a split's fixed costs (its query rows, its
+  // partial output, Combine's read of it) outweigh the parallelism of a
+  // one-tile split.  Tile 64 cuts loop iterations, softmax updates and
+  // barriers per row; short index rows (under 1024 columns) take tile 32 so
+  // that they still split.
   int32_t tile = kv_tile;
-  if (tile == 0) tile = (num_tokens >= cus) ? 64 : 32;
+  if (tile == 0) tile = width >= 1024 ? 64 : 32;
   const int32_t iters = (width + tile - 1) / tile;
   int32_t splits = num_splits;
   if (splits == 0) {
     if (num_tokens >= cus || num_tokens == 0) {
       splits = 1;
     } else {
-      const int32_t want = (2 * cus + num_tokens - 1) / num_tokens;  // ~2 workgroups per CU
-      splits = std::max(1, std::min(want, iters));
+      const int32_t want = (cus + num_tokens - 1) / num_tokens;   // one workgroup per CU
+      splits = std::max(1, std::min(want, iters / 2));
     }
   }
   const int32_t ips = (iters + splits - 1) / splits;

@@ -904,21 +904,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (row >= T * DSA_HEADS) return;
   const int lane = threadIdx.x & 63;
   const int t = row / DSA_HEADS, h = row % DSA_HEADS;
+  // Splits are visited in groups of kU with every load of a group issued
+  // before its arithmetic (a split's weight is exp(lse_s - m), 0 for an empty
+  // split, so no branch depends on a loaded value); splits past S repeat the
+  // last one with weight 0.  The sums run in split order.
+  constexpr int kU = 8;
+  auto lse_at = [&](int s) { return lse_part[(t * ts + int64_t(s) * ss) * DSA_HEADS + h]; };
   float m = kNegInf;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_part[(t * ts + s * ss) * DSA_HEADS + h]);
+  for (int s0 = 0; s0 < S; s0 += kU) {
+    float ls[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) ls[j] = lse_at(min(s0 + j, S - 1));
+#pragma unroll
+    for (int j = 0; j < kU; ++j) m = fmaxf(m, ls[j]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lse_part[(t * ts + s * ss) * DSA_HEADS + h];
-      if (ls == kNegInf) continue;
-      const float wgt = expf(ls - m);
-      tot += wgt;
-      const float4* src = reinterpret_cast<const float4*>(
-          o_part + ((t * ts + s * ss) * DSA_HEADS + h) * DSA_D_LATENT + 8 * lane);
-      const float4 x0 = src[0], x1 = src[1];
-      acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
-      acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
+    for (int s0 = 0; s0 < S; s0 += kU) {
+      float ls[kU];
+      float4 x[kU][2];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int sj = min(s0 + j, S - 1);
+        ls[j] = s0 + j < S ? lse_at(sj) : kNegInf;
+        const float4* src = reinterpret_cast<const float4*>(
+            o_part + ((t * ts + int64_t(sj) * ss) * DSA_HEADS + h) * DSA_D_LATENT + 8 * lane);
+        x[j][0] = src[0];
+        x[j][1] = src[1];
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const float wgt = expf(ls[j] - m);   // exp(-inf) = 0: empty splits add nothing
+        tot += wgt;
+        acc[0] += wgt * x[j][0].x; acc[1] += wgt * x[j][0].y;
+        acc[2] += wgt * x[j][0].z; acc[3] += wgt * x[j][0].w;
+        acc[4] += wgt * x[j][1].x; acc[5] += wgt * x[j][1].y;
+        acc[6] += wgt * x[j][1].z; acc[7] += wgt * x[j][1].w;
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;

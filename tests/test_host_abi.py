@@ -168,11 +168,18 @@ def test_plan_dispatch_uses_query_parallelism():
     # enough query tokens for every CU: one split (no combine work beyond a copy)
     p = dsa.plan_partial(1024, 2048, 0, 0, 256)
     assert p.splits == 1
-    # few tokens: splits supply the parallelism, never more splits than tiles
+    assert p.tile == 64
+    # few tokens: splits supply the parallelism up to one workgroup per CU,
+    # with at least two tiles per split
     p = dsa.plan_partial(8, 2048, 0, 0, 256)
-    assert p.splits > 1 and p.splits * 8 >= 256 and p.splits <= p.iters_total
+    assert (p.tile, p.splits, p.iters_per_split) == (64, 16, 2)
+    p = dsa.plan_partial(100, 2048, 0, 0, 256)
+    assert p.splits == 3 and p.splits * 100 >= 256
+    # a short index row takes tile 32 and still splits
     p = dsa.plan_partial(1, 256, 0, 0, 256)
-    assert p.splits == p.iters_total
+    assert (p.tile, p.splits, p.iters_per_split) == (32, 4, 2)
+    p = dsa.plan_partial(1, 40, 0, 0, 256)
+    assert (p.tile, p.splits) == (32, 1)
     L = dsa.lib()
     out = dsa.PartialPlan()
     assert L.dsa_plan_partial(4, 0, 0, 0, 0, ctypes.byref(out)) == 1
