@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -99,6 +102,16 @@ __device__ __forceinline__ float index_score2(const f32x4& accA, const float (&w
   const float v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
   const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).

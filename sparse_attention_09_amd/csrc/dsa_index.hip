@@ -271,12 +271,34 @@ __device__ __forceinline__ void index_unit(
     __syncthreads();
     cur ^= 1;
   };
-  int pg = page_begin;
-  for (; pg + 1 < page_end; pg += 2) {
-    step(pg, pb, pa);
-    step(pg + 1, pa, pb);
+  if (MODE == kEmit && page_end - page_begin == kPages) {
+    // a whole chunk (the common case): the same steps unrolled with the page
+    // count known, so the last two steps request no page past the chunk, the
+    // last one stages nothing, and the workgroup ends with no load in flight
+    // (the modes that hold score stores keep the loop: unrolled, they spill)
+    dsa::static_for<kPages>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      flush();
+      if constexpr (s + 2 < kPages) {
+        if constexpr (s % 2 == 0) load_page(pa, page_begin + s + 2);
+        else load_page(pb, page_begin + s + 2);
+      }
+      if (wave_active) compute_page(page_begin + s);
+      if constexpr (s + 1 < kPages) {
+        if constexpr (s % 2 == 0) store_page(pb, cur ^ 1);
+        else store_page(pa, cur ^ 1);
+        __syncthreads();
+        cur ^= 1;
+      }
+    });
+  } else {
+    int pg = page_begin;
+    for (; pg + 1 < page_end; pg += 2) {
+      step(pg, pb, pa);
+      step(pg + 1, pa, pb);
+    }
+    if (pg < page_end) step(pg, pb, pa);
   }
-  if (pg < page_end) step(pg, pb, pa);
   flush();
   if constexpr (MODE == kEmit) {
     // each wave writes out its own tokens' LDS slots (the flushes above were

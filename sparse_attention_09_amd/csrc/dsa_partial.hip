@@ -75,16 +75,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order
-template <class F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 struct PartialArgs {
   const uint8_t* latent;
   int num_pages;
@@ -692,7 +682,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
     const uint16_t* kq = kt + klane;
     if constexpr (kPipeQK) {
       u32x4 kn = *reinterpret_cast<const u32x4*>(kq);
-      static_for<kQS>([&](auto KS) {
+      dsa::static_for<kQS>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
         const u32x4 kf = kn;
         if constexpr (ks + 1 < kQS) kn = *reinterpret_cast<const u32x4*>(kq + 32 * (ks + 1));
@@ -716,7 +706,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
             sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
                                              sacc[mb][hb]);
       }
-      static_for<kQS>(stage);
+      dsa::static_for<kQS>(stage);
     }
     // keep head block dh, send head block 1-dh to the partner (wave ^ 2)
     f32x4 sv[kOMB];
