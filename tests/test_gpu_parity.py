@@ -314,3 +314,34 @@ def test_topk_full_rows_candidate_and_fallback_paths():
     for t in range(sc.shape[0]):
         ref = O.topk_positions(sc[t, :int(tok_pos[t]) + 1].numpy(), k)
         assert np.array_equal(idx[t], ref), t
+
+
+@pytest.mark.parametrize("S", [1, 7, 8, 9, 64])
+def test_combine_against_oracle_merge(S):
+    """dsa_combine on seeded partials against the oracle's log-sum-exp merge:
+    split counts around the kernel's group of eight, empty splits (lse -inf,
+    o 0) mixed in, heads whose every split is empty, and lse values far
+    apart.  Only the bf16 rounding of o separates the two."""
+    T = 5
+    g = torch.Generator().manual_seed(100 + S)
+    o = torch.randn((T, S, 64, 512), generator=g, dtype=torch.float64)
+    lse = torch.randn((T, S, 64), generator=g, dtype=torch.float64) * 6.0
+    lse[:, :, 5] += 80.0 * torch.rand((T, S), generator=g, dtype=torch.float64)   # far apart
+    empty = torch.rand((T, S, 64), generator=g) < 0.3
+    empty[:, :, 7] = True                                                          # all splits empty
+    lse[empty] = -np.inf
+    o[empty.unsqueeze(-1).expand_as(o)] = 0.0
+    o32, lse32 = o.to(torch.float32), lse.to(torch.float32)
+    say(f"[case] combine S={S}")
+    out, lse_out = dsa.combine(o32.to(DEV), lse32.to(DEV))
+    torch.cuda.synchronize()
+    got_o = bf16_to_f64(out)
+    got_l = lse_out.cpu().numpy().astype(np.float64)
+    for t in range(T):
+        ref_o, ref_l = O.combine(o32[t].numpy(), lse32[t].numpy())
+        assert np.array_equal(np.isneginf(got_l[t]), np.isneginf(ref_l))
+        fin = np.isfinite(ref_l)
+        assert np.all(got_o[t][~fin] == 0)
+        assert np.max(np.abs(got_l[t][fin] - ref_l[fin])) <= 1e-4
+        err = np.abs(got_o[t][fin] - ref_o[fin])
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref_o[fin]) + 1e-6), f"token {t}: max err {err.max()}"
