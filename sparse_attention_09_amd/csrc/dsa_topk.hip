@@ -525,11 +525,12 @@ __device__ __forceinline__ void minmax256(Sel& s, uint32_t lo, uint32_t hi, uint
 }
 
 // k-th largest of a key multiset spread over the workgroup (1 <= k <= its
-// size; every key in [kmin, kmax]).  Radix selection on d = key - kmin, 8-bit
-// digits from the top bit of kmax - kmin down, so the first digit already
-// spreads the keys.  `each(f)` calls f on every key the calling thread holds.
-// Returns the key; *r_out gets how many keys equal to it belong to the k
-// largest.  Barriers.
+// size; every key in [kmin, kmax]).  Radix selection on d = key - kmin, in
+// digits of 8 bits taken from the top bit of kmax - kmin down (the last digit
+// takes what is left), so the first digit already spreads the keys over the
+// histogram instead of piling them into a few bins.  `each(f)` calls f on
+// every key the calling thread holds.  Returns the key; *r_out gets how many
+// keys equal to it belong to the k largest.  Barriers.
 template <int NT, class Each>
 __device__ __forceinline__ uint32_t radix_select_block(SelT<NT>& s, uint32_t k_rem, uint32_t kmin,
                                                        uint32_t kmax, Each each, uint32_t* r_out) {
@@ -539,17 +540,21 @@ __device__ __forceinline__ uint32_t radix_select_block(SelT<NT>& s, uint32_t k_r
     *r_out = k_rem;
     return kmin;
   }
-  const int passes = (32 - __clz(span) + 7) / 8;
-  uint32_t prefix = 0;   // decided high digits of d
+  const int bits = 32 - __clz(span);
+  const int passes = (bits + 7) / 8;
+  uint32_t prefix = 0;   // decided high bits of d: bits [top, bits)
+  int top = bits;
   if (tid < 256) s.hist[0][tid] = 0;
   __syncthreads();
   for (int pass = 0; pass < passes; ++pass) {
-    const int sh = 8 * (passes - 1 - pass);
+    const int sh = max(top - 8, 0);                  // this digit: bits [sh, top)
+    const uint32_t dmask = (1u << (top - sh)) - 1u;
     uint32_t* h = s.hist[pass & 1];
     if (tid < 256) s.hist[(pass + 1) & 1][tid] = 0;   // the next pass's histogram
     each([&](uint32_t key) {
-      const uint32_t d = (key - kmin) >> sh;
-      if ((d >> 8) == prefix) atomicAdd(&h[d & 255u], 1u);
+      const uint32_t d = key - kmin;
+      const uint32_t hi = top >= 32 ? 0u : d >> top;
+      if (hi == prefix) atomicAdd(&h[(d >> sh) & dmask], 1u);
     });
     __syncthreads();
     if (tid < 64) {
@@ -574,8 +579,9 @@ __device__ __forceinline__ uint32_t radix_select_block(SelT<NT>& s, uint32_t k_r
       }
     }
     __syncthreads();
-    prefix = (prefix << 8) | s.digit;
+    prefix = (prefix << (top - sh)) | s.digit;
     k_rem -= s.above;
+    top = sh;
   }
   *r_out = k_rem;
   return kmin + prefix;
