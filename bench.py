@@ -341,6 +341,20 @@ def main():
     print(f"[bench] plan tile={plan.tile} splits={plan.splits} cus={cus} "
           f"selection={'fused' if path.fused_topk else 'scores+topk'}", file=sys.stderr, flush=True)
 
+    # one step = these calls in order (what DsaPath.step runs)
+    if path.fused_topk:
+        names = ["index_topk"]
+        calls = [lambda: path.index_topk(wl.q_idx, wl.w)]
+    else:
+        names = ["index_scores", "topk"]
+        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk]
+    if path.fused:
+        names += ["partial"]
+        calls += [lambda: path.attend(wl.q)]
+    else:
+        names += ["partial", "combine"]
+        calls += [lambda: path.partial(wl.q), path.combine]
+
     def step():
         path.step(wl.q_idx, wl.w, wl.q)
 
@@ -348,18 +362,37 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # whole-path timing
+    # Timed region: K steps, with an event recorded on the working stream
+    # before the first call and after every call, so the step time and each
+    # kernel's average launch duration come from the same K steps.
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = len(calls)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n + 1)]
     torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        for j, c in enumerate(calls):
+            c()
+            evs[i * n + j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_total = evs[0].elapsed_time(evs[-1])
+    ms_step = ms_total / args.steps
+    acc = {nm: 0.0 for nm in names}
+    for i in range(args.steps):
+        for j, nm in enumerate(names):
+            acc[nm] += evs[i * n + j].elapsed_time(evs[i * n + j + 1])
+    per_us = {nm: 1000.0 * acc[nm] / args.steps for nm in names}
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # the same K steps without the markers between calls (a check that the
+    # markers cost nothing measurable)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_plain = e0.elapsed_time(e1) / args.steps
     ms_graph = None
     if not args.no_graph:
         # the same step recorded once on a HIP graph and replayed (no host
@@ -375,30 +408,6 @@ def main():
         torch.cuda.synchronize()
         ms_graph = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel timing on the same stream (separate loop, events between calls)
-    if path.fused_topk:
-        names = ["index_topk"]
-        calls = [lambda: path.index_topk(wl.q_idx, wl.w)]
-    else:
-        names = ["index_scores", "topk"]
-        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk]
-    if path.fused:
-        names += ["partial"]
-        calls += [lambda: path.attend(wl.q)]
-    else:
-        names += ["partial", "combine"]
-        calls += [lambda: path.partial(wl.q), path.combine]
-    acc = {n: 0.0 for n in names}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        evs[0].record(stream)
-        for i, c in enumerate(calls):
-            c()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            acc[n] += evs[i].elapsed_time(evs[i + 1])
-    per_us = {n: 1000.0 * acc[n] / args.steps for n in names}
     fallback_tokens = path.fallback_count()
     unfused = None
     if path.fused_topk:
@@ -456,6 +465,7 @@ def main():
                    "selection": "fused indexer + top-k" if path.fused_topk
                    else "score matrix + top-k",
                    "launch": "eager calls on one stream"},
+        "ms_per_step_without_markers": round(ms_plain, 4),
         "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
         "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
                 "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
