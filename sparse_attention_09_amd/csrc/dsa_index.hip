@@ -78,7 +78,9 @@ __device__ __forceinline__ void index_unit(
   if (page_end <= page_begin) {
     // only when the page table is shorter than the context: no candidates
     if constexpr (MODE == kEmit)
-      for (int i = tid; i < nq; i += kThreads) em.count[int64_t(t_begin + i) * em.nch + chunk] = 0;
+      for (int i = tid; i < nq; i += kThreads)
+        *reinterpret_cast<int2*>(em.cand + 2 * ((int64_t(t_begin + i) * em.nch + chunk) * em.capr)) =
+            make_int2(0, 0);
     return;
   }
 
@@ -304,23 +306,23 @@ __device__ __forceinline__ void index_unit(
     // each wave writes out its own tokens' LDS slots (the flushes above were
     // its own LDS writes); the count may exceed em.cap: the selection treats
     // that chunk as overflowed
-    // as (score, position) pairs padded to whole 128-byte lines (a line
-    // written in part would make the memory side fetch it first)
+    // after the count, as (score, position) pairs padded to whole 128-byte
+    // lines (a line written in part would make the memory side fetch it first)
     if (wave_active) {
       for (int side = 0; side < (hasB ? 2 : 1); ++side) {
         const int li = 2 * pair + side;
         const int tok = side ? tB : tA;
         const int cnt = side ? cntB : cntA;
         const int n = min(cnt, em.cap);
-        const int m = (n + dsa::kCandAlign - 1) / dsa::kCandAlign * dsa::kCandAlign;
+        const int m = (n + dsa::kCandAlign) / dsa::kCandAlign * dsa::kCandAlign;   // n + 1, whole lines
         int32_t* run = em.cand + 2 * ((int64_t(tok) * em.nch + chunk) * em.capr);
         for (int s2 = lane; s2 < m; s2 += 64) {
-          const bool real = s2 < n;
-          const int32_t v = real ? __float_as_int(cand_v[li * kCandLds + s2]) : 0;
-          const int32_t ps = real ? p_begin + int(cand_p[li * kCandLds + s2]) : -1;
+          const int e = s2 - 1;   // candidate in pair s2
+          const bool real = s2 >= 1 && e < n;
+          const int32_t v = s2 == 0 ? cnt : real ? __float_as_int(cand_v[li * kCandLds + e]) : 0;
+          const int32_t ps = real ? p_begin + int(cand_p[li * kCandLds + e]) : -1;
           *reinterpret_cast<int2*>(run + 2 * s2) = make_int2(v, ps);
         }
-        if (lane == 0) em.count[int64_t(tok) * em.nch + chunk] = cnt;
       }
     }
   }
@@ -364,7 +366,7 @@ dsa_status launch_index(int mode, const dsa_pool* pool, const int32_t* page_tabl
   const uint16_t* keys =
       reinterpret_cast<const uint16_t*>(pool->base + pool->layout.index_plane_offset);
   const dim3 grid{unsigned(chunks), unsigned(num_reqs), unsigned(qblocks)};
-  const IndexEmit none{nullptr, nullptr, nullptr, 0, 0, 0};
+  const IndexEmit none{nullptr, nullptr, 0, 0, 0};
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto go = [&](auto kernel, const IndexEmit& e) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, st, keys, pool->num_pages, page_table,

@@ -44,18 +44,17 @@ constexpr int32_t kIndexMaxCap = 128;       // emit pass: most candidate slots p
 // positions), the scores >= thr[t], in position order, at slots
 // [(t*nch + j)*cap, +cap), and their number (possibly > cap) in
 // count[t*nch + j].
-// Emit-pass output.  Each (token, chunk) has a region of capr pairs (cap
-// rounded up to whole 16-pair, 128-byte lines) and writes its candidates there
-// as (score bits, position) pairs in position order, padded to whole lines so
-// that no line is written in part.
+// Emit-pass output.  Each (token, chunk) has a region of capr pairs (cap + 1
+// rounded up to whole 16-pair, 128-byte lines): pair 0 holds the chunk's
+// candidate count, then its candidates as (score bits, position) pairs in
+// position order, padded to whole lines so that no line is written in part.
 struct IndexEmit {
   const float* thr;
   int32_t* cand;      // pairs: [token][nch][capr][2]
-  int32_t* count;     // [token][nch]
   int32_t nch, cap, capr;
 };
 constexpr int32_t kCandAlign = 16;   // pairs per 128-byte line
-constexpr int32_t cand_cap_rounded(int32_t cap) { return (cap + kCandAlign - 1) / kCandAlign * kCandAlign; }
+constexpr int32_t cand_region_pairs(int32_t cap) { return (cap + kCandAlign) / kCandAlign * kCandAlign; }
 
 // Launches the indexer: mode 0 writes scores[t*ld + p]; mode 1 (sample pass)
 // writes scores[t*ld + 64*s + x] for position 64*32*s + x; mode 2 emits

@@ -659,7 +659,7 @@ struct SelSmem {
 // most k positions are written whole.  Tokens whose candidates cannot be
 // trusted go to the fallback list.
 __global__ __launch_bounds__(kSmallThreads) void select_kernel(
-    const int32_t* __restrict__ tok_pos, int max_ctx, int k, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ tok_pos, int max_ctx, int k,
     const int2* __restrict__ cand, int nch, int cap, int capr, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ nflag, int32_t* __restrict__ flag_list) {
   __shared__ SelSmem sm;
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
   int c = 0;
   bool over = false;
   if (tid < nch_t) {
-    c = count[int64_t(t) * nch + tid];
+    c = cand[(int64_t(t) * nch + tid) * capr].x;   // the region's count pair
     over = c > cap || c < 0;
   }
   uint32_t n;
@@ -699,13 +699,13 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
       const int m = j + step;
       if (m < nch_t && sm.off[m] <= q) j = m;
     }
-    src[u] = q < N ? (int64_t(t) * nch + j) * capr + (q - sm.off[j]) : -1;
+    src[u] = q < N ? (int64_t(t) * nch + j) * capr + 1 + (q - sm.off[j]) : -1;
   }
   // loads unconditional (an unused slot reads the token's first slot) so all
   // are in flight at once; LDS writes after
   float v[kPer];
   int32_t pv[kPer];
-  const int64_t first = int64_t(t) * nch * capr;
+  const int64_t first = int64_t(t) * nch * capr + 1;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int2 x = cand[src[u] >= 0 ? src[u] : first];
@@ -1000,7 +1000,7 @@ namespace {
 // Workspace of the fused path (byte offsets, each 256-aligned).  The fallback
 // counter sits at offset 0.
 struct FusedLayout {
-  size_t nflag, list, samples, thr, count, cand, total;
+  size_t nflag, list, samples, thr, cand, total;
   int ls, nch, capr;
 };
 
@@ -1017,8 +1017,7 @@ FusedLayout fused_layout(int64_t num_tokens, int32_t max_ctx, int32_t cap) {
   L.list = o; o += up(4 * T);
   L.samples = o; o += up(4 * T * size_t(L.ls));
   L.thr = o; o += up(4 * T);
-  L.count = o; o += up(4 * T * size_t(L.nch));
-  L.capr = dsa::cand_cap_rounded(cap);
+  L.capr = dsa::cand_region_pairs(cap);
   L.cand = o; o += up(8 * T * size_t(L.nch) * size_t(L.capr));
   L.total = o;
   return L;
@@ -1065,7 +1064,6 @@ extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_t
   int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
   float* samples = reinterpret_cast<float*>(ws + L.samples);
   float* thr = reinterpret_cast<float*>(ws + L.thr);
-  int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
   int32_t* cand = reinterpret_cast<int32_t*>(ws + L.cand);
   // default: about 2k candidates (within what one selection workgroup holds)
   const int target = cand_target > 0 ? cand_target : std::min(2 * k, kSelMax - 1024);
@@ -1079,14 +1077,14 @@ extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_t
   hipLaunchKernelGGL(threshold_kernel, dim3(num_tokens), dim3(kSmallThreads), 0, st, samples, L.ls,
                      tok_pos, max_ctx, k, target, thr, nflag);
   if (max_ctx > 0) {
-    const dsa::IndexEmit em{thr, cand, count, L.nch, cap, L.capr};
+    const dsa::IndexEmit em{thr, cand, L.nch, cap, L.capr};
     s = dsa::launch_index(2, pool, page_table, pt_stride, q_offsets, num_reqs, max_q, tok_pos,
                           num_tokens, max_ctx, q_idx, w, nullptr, 0, &em, stream);
     if (s != DSA_OK) return s;
   }
   hipLaunchKernelGGL(select_kernel, dim3(num_tokens), dim3(kSmallThreads), 0, st, tok_pos, max_ctx,
-                     k, count, reinterpret_cast<const int2*>(cand), L.nch, cap, L.capr, idx,
-                     nflag, list);
+                     k, reinterpret_cast<const int2*>(cand), L.nch, cap, L.capr, idx, nflag,
+                     list);
   const RowArgs a{nullptr, 0, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
   const IndexIn f{reinterpret_cast<const uint16_t*>(pool->base + pool->layout.index_plane_offset),
                   pool->num_pages, page_table, pt_stride, q_offsets, num_reqs, q_idx, w};

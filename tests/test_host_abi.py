@@ -200,11 +200,11 @@ def test_index_topk_workspace_bytes():
     L = dsa.lib()
     T, cap = 1024, 128
     # fallback counter, fallback list, samples (one page in 32: 32 x 64 columns),
-    # thresholds, counts per 512-chunk (128), candidate (score, position)
-    # pairs: 128 chunks x cap rounded up to whole 16-pair lines
-    want = 256 + 4 * T + 4 * T * 2048 + 4 * T + 4 * T * 128 + 8 * T * 128 * cap
+    # thresholds, and per 512-position chunk (128) a region of (score,
+    # position) pairs: a count pair and cap candidates, in whole 16-pair lines
+    want = 256 + 4 * T + 4 * T * 2048 + 4 * T + 8 * T * 128 * (cap + 16)
     assert L.dsa_index_topk_workspace_bytes(T, 65536, cap) == want
-    want20 = want - 8 * T * 128 * cap + 8 * T * 128 * 32
+    want20 = want - 8 * T * 128 * (cap + 16) + 8 * T * 128 * 32
     assert L.dsa_index_topk_workspace_bytes(T, 65536, 20) == want20
     assert L.dsa_index_topk_workspace_bytes(T, 65537, cap) == 0     # rows too long
     assert L.dsa_index_topk_workspace_bytes(T, 4096, 0) == 0
