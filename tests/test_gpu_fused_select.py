@@ -74,8 +74,10 @@ def test_fused_caps_and_targets(seed):
     pool = make_pool(wl)
     ref = _oracle_idx(wl)
     k = wl.spec.k
-    for cap, target in [(128, 0), (64, 0), (32, 0), (4, 0), (1, 0), (128, k // 8), (128, 4 * k),
-                        (128, 1 << 20), (16, 1 << 20)]:
+    # caps around the 16-pair line of a candidate region (count pair + cap)
+    for cap, target in [(128, 0), (64, 0), (32, 0), (15, 0), (17, 0), (4, 0), (1, 0),
+                        (128, k // 8), (128, 4 * k), (128, 1 << 20), (16, 1 << 20),
+                        (15, 1 << 20)]:
         say(f"[case] fused tiny_fp8 seed={seed} cap={cap} target={target}")
         got, nfb = _fused(wl, pool, cap, target)
         for t in range(wl.num_tokens):
