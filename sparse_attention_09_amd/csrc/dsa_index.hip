@@ -55,8 +55,8 @@ __device__ __forceinline__ void index_unit(
     int pt_stride, const int32_t* __restrict__ q_offsets, const int32_t* __restrict__ tok_pos,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, float* __restrict__ scores,
     int64_t ld, int max_ctx, int num_tokens, const dsa::IndexEmit& em,
-    uint16_t (&lds)[2][DSA_PAGE_TOKENS * kRowBf16], float* cand_v, uint16_t* cand_p, int chunk,
-    int req, int qblock) {
+    uint16_t (&lds)[2][DSA_PAGE_TOKENS * kRowBf16], float* cand_v, uint16_t* cand_p, float* sst,
+    int chunk, int req, int qblock) {
   // the sample pass visits logical pages 0, 32, 64, ... (its "page" pg is the
   // sample page, logical page 32 pg); the other modes visit every page
   constexpr int kStride = MODE == kSample ? kSampleStride : 1;
@@ -136,16 +136,13 @@ __device__ __forceinline__ void index_unit(
   }
   // Lanes of groups 0 and 2 own the scores of token A and token B (the
   // epilogue leaves A's in lanes 0..31 and B's in 32..63): their position
-  // bound, threshold and output row or candidate slots.
+  // bound, threshold and LDS row (score staging or candidate slots).
   const bool owner = g == 0 || g == 2;
   const bool lane_b = g >= 2;
   const int my_pos = lane_b ? posB : posA;
   const float my_thr = lane_b ? thrB : thrA;
-  const int my_t = (lane_b && hasB) ? tB : tA;
-  float* my_row = nullptr;
-  if constexpr (MODE != kEmit) my_row = scores + int64_t(my_t) * ld;
-  // emit pass: candidates of this chunk so far (wave-uniform), and this lane's
-  // token's LDS candidate row
+  // emit pass: candidates of this chunk so far (wave-uniform); this lane's
+  // token's LDS row (its slot in the block)
   int cntA = 0, cntB = 0;
   const int my_li = 2 * pair + ((lane_b && hasB) ? 1 : 0);
 
@@ -183,13 +180,23 @@ __device__ __forceinline__ void index_unit(
   store_page(pa, 0);
   __syncthreads();
   int cur = 0;
-  // scores of the last computed page (not the emit pass, which writes its
-  // candidates to LDS at once): the value of block slot k (block sub + k*nsub)
-  // and the page's first position / output column (held_pos0 < 0: nothing held)
-  float held[4];
-  int held_pos0 = -1, held_col0 = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) held[k] = 0.f;
+  // Scores of a computed page (not the emit pass, which writes its candidates
+  // to LDS at once) go to the LDS staging sst[parity][token slot][64] and are
+  // stored at the start of the next step, after its barrier, by threads
+  // 0..127: each takes 4 consecutive positions of one token, so a token's
+  // page leaves as whole 16-byte pieces (two full 128-byte lines) instead of
+  // 4-byte stores.  held_pos0 / held_col0: the held page's first position and
+  // output column (held_pos0 < 0: nothing held); par: the parity computed next.
+  int held_pos0 = -1, held_col0 = 0, par = 0;
+  const int fslot = tid >> 4, fgrp = tid & 15;   // flush: token slot, 4-position group
+  int fpos = -1;
+  float* frow = nullptr;
+  if constexpr (MODE != kEmit) {
+    if (tid < kQB * 16 && fslot < nq) {
+      fpos = min(tok_pos[t_begin + fslot], max_ctx - 1);
+      frow = scores + int64_t(t_begin + fslot) * ld;
+    }
+  }
   // scores (or candidates) of page pg, read from LDS buffer `cur`
   auto compute_page = [&](int pg) {
     const int pos0 = pg * kStride * DSA_PAGE_TOKENS;
@@ -212,7 +219,9 @@ __device__ __forceinline__ void index_unit(
       // lanes 0..31: token A's scores, lanes 32..63: token B's; lanes of
       // groups 0 and 2 own position c of the block
       const float sc = dsa::index_score2(accA, wa, accB, wb);
-      if constexpr (MODE != kEmit) held[k] = sc;
+      if constexpr (MODE != kEmit) {
+        if (owner && (!lane_b || hasB)) sst[(par * kQB + my_li) * DSA_PAGE_TOKENS + nb * 16 + c] = sc;
+      }
       if constexpr (MODE == kEmit) {
         // slots follow the ballot order, i.e. position order
         const int p = pos0 + nb * 16 + c;
@@ -242,19 +251,28 @@ __device__ __forceinline__ void index_unit(
     } else {
       block(0, sub);
     }
-    held_pos0 = pos0;
-    held_col0 = col0;
+    (void)col0;
   };
-  // stores the held outputs (wave-uniform: held_pos0 is the same in all lanes)
+  // the page a step computes (workgroup-uniform): what the next flush stores
+  auto hold = [&](int pg) {
+    held_pos0 = pg * kStride * DSA_PAGE_TOKENS;
+    held_col0 = MODE == kSample ? pg * DSA_PAGE_TOKENS : held_pos0;
+  };
+  // stores the held page's visible scores (after the barrier that ends the
+  // step which computed them)
   auto flush = [&]() {
-    if (held_pos0 < 0) return;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < 4 / nsub) {
-        const int nb = sub + k * nsub;
-        const int p = held_pos0 + nb * 16 + c;
-        if constexpr (MODE != kEmit) {
-          if (owner && p <= my_pos) my_row[held_col0 + nb * 16 + c] = held[k];
+    if constexpr (MODE != kEmit) {
+      if (held_pos0 >= 0 && frow != nullptr) {
+        const int p0 = held_pos0 + 4 * fgrp;
+        const float4 v = *reinterpret_cast<const float4*>(
+            sst + ((par ^ 1) * kQB + fslot) * DSA_PAGE_TOKENS + 4 * fgrp);
+        float* dst = frow + held_col0 + 4 * fgrp;
+        if (p0 + 3 <= fpos) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          if (p0 <= fpos) dst[0] = v.x;
+          if (p0 + 1 <= fpos) dst[1] = v.y;
+          if (p0 + 2 <= fpos) dst[2] = v.z;
         }
       }
     }
@@ -269,9 +287,11 @@ __device__ __forceinline__ void index_unit(
     flush();
     load_page(fill, min(pg + 2, page_end - 1));
     if (wave_active) compute_page(pg);
+    hold(pg);
     store_page(next, cur ^ 1);
     __syncthreads();
     cur ^= 1;
+    par ^= 1;
   };
   if (MODE == kEmit && page_end - page_begin == kPages) {
     // a whole chunk (the common case): the same steps unrolled with the page
@@ -342,8 +362,11 @@ __global__ __launch_bounds__(kThreads, 4) void index_kernel(
   // start), written to memory once at the end
   __shared__ float cand_v[MODE == kEmit ? kQB * kCandLds : 1];
   __shared__ uint16_t cand_p[MODE == kEmit ? kQB * kCandLds : 1];
+  // scores and sample passes: the last computed page's scores, per parity
+  __shared__ __attribute__((aligned(16))) float sst[MODE != kEmit ? 2 * kQB * DSA_PAGE_TOKENS : 4];
   index_unit<MODE>(keys, num_pages, page_table, pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld,
-                   max_ctx, num_tokens, em, lds, cand_v, cand_p, blockIdx.x, blockIdx.y, blockIdx.z);
+                   max_ctx, num_tokens, em, lds, cand_v, cand_p, sst, blockIdx.x, blockIdx.y,
+                   blockIdx.z);
 }
 
 }  // namespace
