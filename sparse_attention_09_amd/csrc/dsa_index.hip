@@ -172,8 +172,8 @@ __device__ __forceinline__ void index_unit(
   // The memory schedule keeps every step straight-line, so the compiler's
   // wait before staging a page counts exactly the four younger prefetch
   // loads: prefetches are unconditional (past the range they repeat the last
-  // page), the idle LDS buffer is always written, and a step's outputs are
-  // held in registers and stored at the start of the next step, before its
+  // page), the idle LDS buffer is always written, and a step's scores are
+  // held in LDS and stored at the start of the next step, before its
   // prefetch.
   load_page(pa, page_begin);
   load_page(pb, min(page_begin + 1, page_end - 1));
