@@ -33,6 +33,18 @@
  *   - Every argument is validated on the host before anything is enqueued; on
  *     an error nothing is launched, the status is returned and a message is
  *     kept for dsa_last_error() (thread-local).
+ *   - Page ids and token positions in device memory are trusted: a kernel
+ *     clamps an out-of-range page id into the pool rather than fault.  With
+ *     the environment variable DSA_VALIDATE=1, the calls that read the page
+ *     table (dsa_index_scores, dsa_index_topk, dsa_sparse_mla_partial,
+ *     dsa_sparse_mla) first wait for the work queued on `stream`, copy
+ *     q_offsets, tok_pos and the page table to the host and check that
+ *     q_offsets runs from 0 to num_tokens without decreasing, that every
+ *     tok_pos is in [-1, pt_stride*64) and that every page id a token can
+ *     reach (logical pages 0 .. tok_pos/64 of its request) is in
+ *     [0, num_pages); otherwise they return DSA_ERR_INVALID_ARG and launch
+ *     nothing.  A debugging aid: it synchronizes, so it is not for graph
+ *     capture or timing.
  *   - Model dimensions are fixed: 64 heads, latent 512 + rope 64 (q/k dim
  *     576, v dim 512), indexer 16 heads x 128, 64-token pages.
  *   - bf16 values are passed as uint16_t bit patterns.

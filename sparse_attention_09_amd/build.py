@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_host.cpp", "dsa_index.hip", "dsa_topk.hip", "dsa_partial.hip", "dsa_append.hip"]
+SOURCES = ["dsa_host.cpp", "dsa_validate.cpp", "dsa_runtime.hip", "dsa_index.hip", "dsa_topk.hip",
+           "dsa_partial.hip", "dsa_append.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -105,15 +105,9 @@ extern "C" dsa_status dsa_kv_append(const dsa_pool* pool, const int32_t* page_ta
                                     int32_t pt_stride, int32_t num_reqs, const int32_t* req,
                                     const int32_t* pos, int32_t n, const uint16_t* latent,
                                     const uint16_t* keys, void* stream) {
-  if (!pool) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: pool is null");
-  if (n < 0 || num_reqs < 0 || pt_stride < 1)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: need n >= 0, num_reqs >= 0, pt_stride >= 1");
-  if (n == 0) return dsa::ok();
-  if (!page_table || !req || !pos || !latent)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: page_table, req, pos and latent must be non-null");
-  if (!dsa::aligned(latent, 16) || (keys && !dsa::aligned(keys, 16)) || !dsa::aligned(req, 4) ||
-      !dsa::aligned(pos, 4) || !dsa::aligned(page_table, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_kv_append: latent and keys must be 16-byte aligned");
+  const dsa_status s =
+      dsa::check_kv_append(pool, page_table, pt_stride, num_reqs, req, pos, n, latent, keys);
+  if (s != DSA_OK || n == 0) return s == DSA_OK ? dsa::ok() : s;
   uint8_t* lat = reinterpret_cast<uint8_t*>(pool->base + pool->layout.latent_plane_offset);
   uint8_t* kp = reinterpret_cast<uint8_t*>(pool->base + pool->layout.index_plane_offset);
   const dim3 grid{unsigned((n + kRowsPerBlock - 1) / kRowsPerBlock)};

@@ -49,22 +49,6 @@ bool fill_layout(int32_t kv_dtype, int32_t num_pages, dsa_pool_layout* out) {
   return true;
 }
 
-dsa_status check_batch(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
-                       const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
-                       int32_t num_tokens, const char* who) {
-  std::string w(who);
-  if (!pool) return fail(DSA_ERR_INVALID_ARG, w + ": pool is null");
-  if (num_tokens < 0 || num_reqs < 0) return fail(DSA_ERR_INVALID_ARG, w + ": negative size");
-  if (num_tokens == 0) return DSA_OK;
-  if (num_reqs < 1) return fail(DSA_ERR_INVALID_ARG, w + ": tokens without requests");
-  if (!page_table || !q_offsets || !tok_pos)
-    return fail(DSA_ERR_INVALID_ARG, w + ": page_table, q_offsets and tok_pos must be non-null");
-  if (pt_stride < 1) return fail(DSA_ERR_INVALID_ARG, w + ": pt_stride must be >= 1");
-  if (!aligned(page_table, 4) || !aligned(q_offsets, 4) || !aligned(tok_pos, 4))
-    return fail(DSA_ERR_INVALID_ARG, w + ": int32 arrays must be 4-byte aligned");
-  return DSA_OK;
-}
-
 int32_t topk_num_segments(int32_t max_ctx) {
   return max_ctx <= kTopkSeg ? 1 : (max_ctx + kTopkSeg - 1) / kTopkSeg;
 }

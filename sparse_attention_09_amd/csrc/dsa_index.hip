@@ -410,18 +410,12 @@ extern "C" dsa_status dsa_index_scores(const dsa_pool* pool, const int32_t* page
                                        int32_t num_reqs, int32_t max_q, const int32_t* tok_pos,
                                        int32_t num_tokens, int32_t max_ctx, const uint16_t* q_idx,
                                        const float* w, float* scores, int64_t ld, void* stream) {
-  dsa_status s = dsa::check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
-                                  num_tokens, "dsa_index_scores");
+  dsa_status s = dsa::check_index_scores(pool, page_table, pt_stride, q_offsets, num_reqs, max_q,
+                                         tok_pos, num_tokens, max_ctx, q_idx, w, scores, ld);
+  if (s != DSA_OK || num_tokens == 0 || max_ctx == 0) return s == DSA_OK ? dsa::ok() : s;
+  s = dsa::deep_check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos, num_tokens,
+                            "dsa_index_scores", stream);
   if (s != DSA_OK) return s;
-  if (num_tokens == 0 || max_ctx == 0) return dsa::ok();
-  if (max_q < 1 || max_ctx < 0)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: need max_q >= 1 and max_ctx >= 0");
-  if (!q_idx || !w || !scores)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: q_idx, w and scores must be non-null");
-  if (!dsa::aligned(q_idx, 16) || !dsa::aligned(w, 4) || !dsa::aligned(scores, 16))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: q_idx/scores must be 16-byte aligned");
-  if (ld < max_ctx || ld % 4 != 0)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_scores: need ld >= max_ctx and ld % 4 == 0");
   return dsa::launch_index(kScores, pool, page_table, pt_stride, q_offsets, num_reqs, max_q, tok_pos,
                            num_tokens, max_ctx, q_idx, w, scores, ld, nullptr, stream);
 }

@@ -953,25 +953,16 @@ static dsa_status run_partial(const char* who, const dsa_pool* pool, const int32
                               int32_t num_splits, float* o_part, float* lse_part, uint16_t* out,
                               float* lse_out, void* stream) {
   const std::string w(who);
-  dsa_status s = dsa::check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
-                                  num_tokens, who);
-  if (s != DSA_OK) return s;
-  if (width < 1) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": width must be >= 1");
-  if (kv_tile != 32 && kv_tile != 64 && kv_tile != 128)
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": kv_tile must be 32, 64 or 128");
-  if (num_splits < 1 || num_splits > 65535)
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": num_splits must be in [1, 65535]");
-  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": sm_scale must be finite and > 0");
-  if (num_tokens == 0) return dsa::ok();
   const bool final_out = num_splits == 1 && (out != nullptr || lse_out != nullptr);
-  if (!q || !idx || (final_out ? (!out || !lse_out) : (!o_part || !lse_part)))
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": q, idx and the outputs must be non-null");
-  if (!dsa::aligned(q, 16) || !dsa::aligned(idx, 4) ||
-      (final_out ? !dsa::aligned(out, 4) || !dsa::aligned(lse_out, 4)
-                 : !dsa::aligned(o_part, 16) || !dsa::aligned(lse_part, 4)))
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": q must be 16-byte aligned, o_part 16-byte, "
-                                              "out/lse 4-byte");
+  dsa_status s = dsa::check_partial(who, pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
+                                    num_tokens, q, idx, width, sm_scale, kv_tile, num_splits,
+                                    final_out, final_out ? static_cast<const void*>(out) : o_part,
+                                    final_out ? static_cast<const void*>(lse_out) : lse_part);
+  if (s != DSA_OK) return s;
+  if (num_tokens == 0) return dsa::ok();
+  s = dsa::deep_check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos, num_tokens,
+                            who, stream);
+  if (s != DSA_OK) return s;
   dsa_partial_plan plan;
   if (dsa_plan_partial(num_tokens, width, kv_tile, num_splits, 0, &plan) != DSA_OK)
     return DSA_ERR_INVALID_ARG;
@@ -1045,17 +1036,9 @@ static dsa_status run_combine(const char* who, const float* o_part, const float*
                               int32_t num_tokens, int32_t parts, bool shard_major, uint16_t* out,
                               float* lse, void* stream) {
   const std::string w(who);
-  if (num_tokens < 0) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": num_tokens < 0");
-  if (parts < 1) return dsa::fail(DSA_ERR_INVALID_ARG, w + ": the part count must be >= 1");
-  if (num_tokens == 0) return dsa::ok();
-  if (!o_part || !lse_part || !out || !lse)
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": pointers must be non-null");
-  if (!dsa::aligned(o_part, 16) || !dsa::aligned(out, 16) || !dsa::aligned(lse_part, 4) ||
-      !dsa::aligned(lse, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, w + ": o_part and out must be 16-byte aligned");
+  const dsa_status s = dsa::check_combine(who, o_part, lse_part, num_tokens, parts, out, lse);
+  if (s != DSA_OK || num_tokens == 0) return s == DSA_OK ? dsa::ok() : s;
   const int64_t rows = int64_t(num_tokens) * DSA_HEADS;
-  if ((rows + 3) / 4 > 0x7fffffff)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, w + ": too many tokens for one launch");
   const int64_t ts = shard_major ? 1 : parts, ss = shard_major ? num_tokens : 1;
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), o_part, lse_part, num_tokens, parts, ts, ss,

@@ -763,8 +763,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
 // the union of those lists (a position outside its shard's list is beaten by k
 // positions of that shard already), so one exact selection over at most G*k
 // candidates under the same rule gives it.  One 1024-thread workgroup per token.
-constexpr int kMergeMax = 16384;      // G*k candidates held in LDS
-constexpr int kMaxShards = 16;
+constexpr int kMergeMax = dsa::kDcpMergeMax;     // G*k candidates held in LDS
 
 constexpr int kMergeThreads = 1024;
 using MSel = SelT<kMergeThreads>;
@@ -955,18 +954,12 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(RowArgs a, IndexIn f
 extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos,
                                int32_t num_tokens, int32_t max_ctx, int32_t k, int32_t* idx,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_tokens < 0 || max_ctx < 0) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: negative size");
-  if (k < 1) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: k must be >= 1");
-  if (k > dsa::kTopkMaxK) return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_topk: k above 16384");
+  dsa_status s = dsa::check_topk("dsa_topk", scores, ld, tok_pos, num_tokens, max_ctx, k, idx);
+  if (s != DSA_OK) return s;
   if (num_tokens == 0) return dsa::ok();
-  if (!scores || !tok_pos || !idx)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: scores, tok_pos and idx must be non-null");
-  if (!dsa::aligned(scores, 16) || !dsa::aligned(tok_pos, 4) || !dsa::aligned(idx, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: scores must be 16-byte aligned");
-  if (ld < max_ctx || ld % 4 != 0)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: need ld >= max_ctx and ld % 4 == 0");
-  if (num_tokens > 65535 && max_ctx > kSeg)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_topk: too many long rows for one launch");
+  s = dsa::check_workspace("dsa_topk", workspace, workspace_bytes,
+                           dsa_topk_workspace_bytes(num_tokens, max_ctx, k));
+  if (s != DSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (max_ctx <= kSeg) {
     const RowArgs a{scores, ld, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
@@ -974,14 +967,6 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* t
   } else {
     const int nseg = dsa::topk_num_segments(max_ctx);
     const int kc = (k + 3) & ~3;
-    if (int64_t(nseg) * kc > kSeg)
-      return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_topk: segments x k exceeds one merge workgroup");
-    const size_t need = size_t(num_tokens) * nseg * kc * 8;
-    if (!workspace || workspace_bytes < need)
-      return dsa::fail(DSA_ERR_WORKSPACE, "dsa_topk: workspace of " + std::to_string(need) +
-                                              " bytes required");
-    if (!dsa::aligned(workspace, 256))
-      return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_topk: workspace must be 256-byte aligned");
     float* cv = static_cast<float*>(workspace);
     int32_t* cp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                              size_t(num_tokens) * nseg * kc * 4);
@@ -995,39 +980,9 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* t
   return dsa::ok();
 }
 
-namespace {
-
-// Workspace of the fused path (byte offsets, each 256-aligned).  The fallback
-// counter sits at offset 0.
-struct FusedLayout {
-  size_t nflag, list, samples, thr, cand, total;
-  int ls, nch, capr;
-};
-
-FusedLayout fused_layout(int64_t num_tokens, int32_t max_ctx, int32_t cap) {
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  FusedLayout L{};
-  const int64_t pages = (int64_t(max_ctx) + DSA_PAGE_TOKENS - 1) / DSA_PAGE_TOKENS;
-  const int64_t spages = (pages + dsa::kIndexSampleStride - 1) / dsa::kIndexSampleStride;
-  L.ls = int(spages * DSA_PAGE_TOKENS);
-  L.nch = int((int64_t(max_ctx) + dsa::kIndexChunk - 1) / dsa::kIndexChunk);
-  const size_t T = size_t(num_tokens);
-  size_t o = 0;
-  L.nflag = o; o += up(4);
-  L.list = o; o += up(4 * T);
-  L.samples = o; o += up(4 * T * size_t(L.ls));
-  L.thr = o; o += up(4 * T);
-  L.capr = dsa::cand_region_pairs(cap);
-  L.cand = o; o += up(8 * T * size_t(L.nch) * size_t(L.capr));
-  L.total = o;
-  return L;
-}
-
-}  // namespace
-
 extern "C" size_t dsa_index_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t cap) {
   if (num_tokens <= 0 || max_ctx < 0 || max_ctx > kSeg || cap < 1 || cap > dsa::kIndexMaxCap) return 0;
-  return fused_layout(num_tokens, max_ctx, cap).total;
+  return dsa::fused_layout(num_tokens, max_ctx, cap).total;
 }
 
 extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table,
@@ -1036,29 +991,14 @@ extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_t
                                      int32_t max_ctx, const uint16_t* q_idx, const float* w,
                                      int32_t k, int32_t cap, int32_t cand_target, int32_t* idx,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  dsa_status s = dsa::check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
-                                  num_tokens, "dsa_index_topk");
+  dsa_status s = dsa::check_index_topk(pool, page_table, pt_stride, q_offsets, num_reqs, max_q,
+                                       tok_pos, num_tokens, max_ctx, q_idx, w, k, cap, cand_target,
+                                       idx, workspace, workspace_bytes);
+  if (s != DSA_OK || num_tokens == 0) return s == DSA_OK ? dsa::ok() : s;
+  s = dsa::deep_check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos, num_tokens,
+                            "dsa_index_topk", stream);
   if (s != DSA_OK) return s;
-  if (k < 1 || k > dsa::kTopkMaxK)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need 1 <= k <= 16384");
-  if (cap < 1 || cap > dsa::kIndexMaxCap || cand_target < 0)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need 1 <= cap <= 128 and cand_target >= 0");
-  if (max_q < 1 || max_ctx < 0)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: need max_q >= 1 and max_ctx >= 0");
-  if (max_ctx > kSeg)
-    return dsa::fail(DSA_ERR_UNSUPPORTED,
-                     "dsa_index_topk: rows above 65,536 positions need dsa_index_scores + dsa_topk");
-  if (num_tokens == 0) return dsa::ok();
-  if (!q_idx || !w || !idx)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: q_idx, w and idx must be non-null");
-  if (!dsa::aligned(q_idx, 16) || !dsa::aligned(w, 4) || !dsa::aligned(idx, 4))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: q_idx must be 16-byte aligned");
-  const FusedLayout L = fused_layout(num_tokens, max_ctx, cap);
-  if (!workspace || workspace_bytes < L.total)
-    return dsa::fail(DSA_ERR_WORKSPACE, "dsa_index_topk: workspace of " + std::to_string(L.total) +
-                                            " bytes required");
-  if (!dsa::aligned(workspace, 256))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_index_topk: workspace must be 256-byte aligned");
+  const dsa::FusedLayout L = dsa::fused_layout(num_tokens, max_ctx, cap);
   char* ws = static_cast<char*>(workspace);
   int32_t* nflag = reinterpret_cast<int32_t*>(ws + L.nflag);
   int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
@@ -1099,18 +1039,9 @@ extern "C" dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_t
 extern "C" dsa_status dsa_dcp_merge(int32_t num_shards, int32_t num_tokens, int32_t k,
                                     const int32_t* local_idx, const float* local_scores,
                                     int64_t ld, int32_t* idx, int32_t* shard_idx, void* stream) {
-  if (num_shards < 1 || num_shards > kMaxShards)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need 1 <= num_shards <= 16");
-  if (num_tokens < 0 || k < 1)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need num_tokens >= 0 and k >= 1");
-  if (int64_t(num_shards) * k > kMergeMax)
-    return dsa::fail(DSA_ERR_UNSUPPORTED, "dsa_dcp_merge: num_shards * k above 16384");
-  if (num_tokens == 0) return dsa::ok();
-  if (!local_idx || !local_scores || !idx)
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: local_idx, local_scores and idx must be non-null");
-  if (ld < 1 || !dsa::aligned(local_idx, 4) || !dsa::aligned(local_scores, 4) ||
-      !dsa::aligned(idx, 4) || (shard_idx && !dsa::aligned(shard_idx, 4)))
-    return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_dcp_merge: need ld >= 1 and 4-byte aligned arrays");
+  const dsa_status s = dsa::check_dcp_merge(num_shards, num_tokens, k, local_idx, local_scores, ld,
+                                            idx, shard_idx);
+  if (s != DSA_OK || num_tokens == 0) return s == DSA_OK ? dsa::ok() : s;
   hipLaunchKernelGGL(dcp_merge_kernel, dim3(num_tokens), dim3(kMergeThreads), 0,
                      static_cast<hipStream_t>(stream), num_shards, num_tokens, k, local_idx,
                      local_scores, ld, idx, shard_idx);

@@ -47,9 +47,37 @@ def test_full_path_small(name):
     _check_full_path(_gen(name))
 
 
-@pytest.mark.parametrize("tile,splits", [(32, 1), (32, 3), (64, 1), (64, 2), (32, 40)])
+@pytest.mark.parametrize("tile,splits", [(32, 1), (32, 3), (64, 1), (64, 2), (32, 40), (128, 1),
+                                         (128, 3)])
 def test_full_path_tiles_and_splits(tile, splits):
     _check_full_path(_gen("tiny_fp8", seed=1), tile, splits)
+
+
+@pytest.mark.parametrize("tile,splits", [(128, 1), (128, 2), (64, 2)])
+def test_bf16_partial_splits_against_oracle(tile, splits):
+    # BF16 rows at tile 128 (the kernel stages part of each 128-row tile
+    # separately for the wider rows), with one and with several splits: every
+    # split's (o, lse) and the combined output against the oracle
+    wl = _gen("tiny_bf16", seed=12)
+    hv = HostView(wl)
+    pool = make_pool(wl)
+    for width in (300, 129):
+        say(f"[case] bf16 partial width={width} tile={tile} splits={splits}")
+        idx = synth.random_index(wl.tok_pos, width, seed=width + 7 * tile + splits).to(DEV)
+        o_p, lse_p = dsa.sparse_mla_partial(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q, idx,
+                                            wl.spec.sm_scale, tile, splits)
+        out, lse = dsa.combine(o_p, lse_p)
+        torch.cuda.synchronize()
+        o_p = o_p.cpu().numpy().astype(np.float64)
+        lse_p = lse_p.cpu().numpy().astype(np.float64)
+        out_h, lse_h = bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+        idx_h = idx.cpu().numpy()
+        for t in range(wl.num_tokens):
+            ref = hv.token(t, tile, splits, idx=idx_h[t])
+            for s in range(splits):
+                check_attention(o_p[t, s], lse_p[t, s], ref["o_part"][s], ref["lse_part"][s],
+                                f"token {t} split {s}")
+            check_attention(out_h[t], lse_h[t], ref["o"], ref["lse"], f"token {t}")
 
 
 def test_width_2112_figure4_shape():
@@ -106,13 +134,15 @@ def test_partial_peaked_softmax_and_single_rows():
 
 def test_partial_later_tile_far_above_first_tile():
     # One row of request 1 gets a score about 200 (natural units, sm_scale 1)
-    # above everything in the first tile of the index: at tile 32 the kernel's
-    # reference max, fixed by the first tile, is far too low, and the split
-    # must be recomputed with the exact max.  At tile 64 the row is in the
-    # first tile.  Both must match the oracle.
+    # above everything before it in the index, and it sits at index column
+    # 152: in the fifth tile at tile 32, the third at tile 64 and the second
+    # at tile 128.  The tile-32/64 kernel's reference max, fixed by the first
+    # tile, is then far too low and the split is recomputed with the exact max;
+    # the tile-128 kernel's running max grows by more than its rescale
+    # threshold and O is rescaled.  Every form must match the oracle.
     wl = synth.generate(synth.spec("tiny_bf16"), seed=7, device="cpu")
     b, t, p_hi = 1, 3, 120
-    assert int(wl.tok_req[t]) == b and int(wl.tok_pos[t]) >= 131
+    assert int(wl.tok_req[t]) == b and int(wl.tok_pos[t]) >= 300
     q = O.bf16_bits_to_f64(wl.q[t].view(torch.uint16).numpy())          # [64, 576]
     v = q.sum(axis=0)
     assert (q @ v).min() > 0
@@ -124,18 +154,19 @@ def test_partial_later_tile_far_above_first_tile():
     wl = wl.to(DEV)
     hv = HostView(wl)
     hv.sm_scale = 1.0
-    cols = np.concatenate([np.arange(32), np.arange(100, 132)]).astype(np.int32)
+    cols = np.concatenate([np.arange(32), np.arange(200, 300), np.arange(100, 132)]).astype(np.int32)
+    assert int(np.nonzero(cols == p_hi)[0][0]) == 152
     idx = torch.from_numpy(np.tile(cols, (wl.num_tokens, 1))).to(DEV)
     pool = make_pool(wl)
-    for tile in (32, 64):
-        say(f"[case] partial tile={tile}: dominant row in the second half of the index")
+    for tile, splits in ((32, 1), (64, 1), (128, 1), (128, 2)):
+        say(f"[case] partial tile={tile} splits={splits}: dominant row at index column 152")
         o_p, lse_p = dsa.sparse_mla_partial(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q,
-                                            idx, 1.0, tile, 1)
+                                            idx, 1.0, tile, splits)
         out, lse = dsa.combine(o_p, lse_p)
         torch.cuda.synchronize()
         out_h, lse_h = bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
         for tt in range(wl.num_tokens):
-            ref = hv.token(tt, tile, 1, idx=cols)
+            ref = hv.token(tt, tile, splits, idx=cols)
             check_attention(out_h[tt], lse_h[tt], ref["o"], ref["lse"], f"tile {tile} token {tt}")
             if tt == t:   # the case is what it claims: every head's max is the planted row
                 assert np.all(ref["lse"] > 200)
@@ -196,6 +227,58 @@ def test_kv_append_matches_oracle_bytes(name):
     got = dev.pool.cpu().numpy()
     bad = np.nonzero(got != pool_host.buf)[0]
     assert bad.size == 0, f"{bad.size} pool bytes differ, first at {bad[:8]}"
+
+
+def test_kv_append_rounds_midpoints_to_even_codes():
+    # Values that land exactly halfway between two E4M3FN codes after the
+    # division by the group scale, so the rounding rule decides them: each
+    # group's amax is 448 * 2^e (scale exactly 2^e) and its other 63 values
+    # are +-midpoints * 2^e, covering the midpoints of every adjacent pair of
+    # finite codes (lower code even and odd; subnormal, subnormal-to-normal
+    # and normal range).  Ties go to the even code: the GPU's bytes must equal
+    # the oracle's and the hand-derived codes.
+    wl = synth.generate(synth.spec("tiny_fp8"), seed=9, device="cpu")
+    vals = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).double()  # ascending
+    mids = (vals[:-1] + vals[1:]) / 2                                   # 126 midpoints
+    even_code = torch.where(torch.arange(126) % 2 == 0, torch.arange(126), torch.arange(126) + 1)
+    g = torch.Generator().manual_seed(123)
+    rows, want = [], []
+    for r in range(8):
+        row, wrow = [], []
+        for grp in range(9):
+            e = int(torch.randint(-12, 9, (1,), generator=g))
+            pick = torch.randint(0, 126, (63,), generator=g)
+            if r < 2:                                   # the first rows walk every midpoint
+                pick = (torch.arange(63) + 63 * ((2 * r + grp) % 2)) % 126
+            sign = torch.where(torch.rand(63, generator=g) < 0.5, -1.0, 1.0).double()
+            x = torch.cat([torch.tensor([448.0]).double(), sign * mids[pick]]) * 2.0 ** e
+            codes = torch.cat([torch.tensor([0x7E]), even_code[pick] | torch.where(sign < 0, 0x80, 0)])
+            perm = torch.randperm(64, generator=g)
+            row.append(x[perm])
+            wrow.append(codes[perm])
+        rows.append(torch.cat(row))
+        want.append(torch.cat(wrow))
+    lat = torch.stack(rows)
+    assert torch.equal(lat.to(torch.bfloat16).double(), lat)           # exact in bf16
+    n = lat.shape[0]
+    req = torch.zeros(n, dtype=torch.int32)
+    pos = torch.arange(100, 100 + n, dtype=torch.int32)
+    pool_host = O.PoolView(wl.pool.numpy().copy(), wl.num_pages, wl.spec.kv_dtype)
+    O.append_rows(pool_host, wl.page_table.numpy(), req.tolist(), pos.tolist(),
+                  lat.to(torch.bfloat16).float().numpy(), None)
+    dev = wl.to(DEV)
+    pool = make_pool(dev)
+    say(f"[case] kv_append midpoints: {n} rows")
+    dsa.kv_append(pool, dev.page_table, req.to(DEV), pos.to(DEV), lat.to(torch.bfloat16).to(DEV))
+    torch.cuda.synchronize()
+    got = dev.pool.cpu().numpy()
+    bad = np.nonzero(got != pool_host.buf)[0]
+    assert bad.size == 0, f"{bad.size} pool bytes differ, first at {bad[:8]}"
+    pt = wl.page_table.numpy()
+    for i in range(n):
+        phys = int(pt[0, int(pos[i]) // 64]) * 64 + int(pos[i]) % 64
+        codes = got[phys * 640: phys * 640 + 576]
+        assert np.array_equal(codes, want[i].numpy().astype(np.uint8)), f"row {i}"
 
 
 def test_all_masked_token_gives_zero_and_neg_inf():
