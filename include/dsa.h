@@ -27,7 +27,9 @@
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless the argument says "host".
  *   - The caller owns all device memory (allocated with PyTorch or hipMalloc);
- *     the library never allocates device memory and never synchronizes.
+ *     the library never allocates device memory and never synchronizes (its
+ *     one device buffer of its own, the scratch of dsa_topk_noalloc, is a
+ *     static array of the code object, not an allocation).
  *   - Compute entry points only enqueue work on `stream` (a hipStream_t passed
  *     as void*, NULL = the default stream); DSA_OK means "enqueued".
  *   - Every argument is validated on the host before anything is enqueued; on
@@ -186,6 +188,22 @@ size_t dsa_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t k);
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos, int32_t num_tokens,
                     int32_t max_ctx, int32_t k, int32_t* idx, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* Allocation-free top-k, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): dsa_topk without the workspace argument.  The long-row
+ * staging (rows above 65,536 positions: dsa_topk_workspace_bytes(num_tokens,
+ * max_ctx, k) bytes) lives in a library-owned device array of
+ * DSA_TOPK_SCRATCH_BYTES per GPU, held until the process ends; a call that
+ * needs more returns DSA_ERR_WORKSPACE (e.g. 1,048,576-position rows at
+ * k = 2048 fit 64 tokens per call).  The call allocates nothing.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from several threads) race and must be ordered by
+ * the caller.  Results are bit for bit those of dsa_topk. */
+#define DSA_TOPK_SCRATCH_BYTES (16u << 20)
+dsa_status dsa_topk_noalloc(const float* scores, int64_t ld, const int32_t* tok_pos,
+                            int32_t num_tokens, int32_t max_ctx, int32_t k, int32_t* idx,
+                            void* stream);
 
 /* Fused indexer + top-k [LMSYS-1 indexer and selection; the blog's "top-k
  * v2" change; the fused selection is this library's design]: the same idx as

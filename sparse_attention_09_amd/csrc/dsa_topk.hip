@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -951,6 +953,36 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(RowArgs a, IndexIn f
 
 }  // namespace
 
+namespace {
+
+// The launches of one top-k call; the long-row staging (candidate scores and
+// positions of every token and segment) is at cand, already checked to hold
+// dsa_topk_workspace_bytes(num_tokens, max_ctx, k) bytes.
+dsa_status launch_topk(const char* who, const float* scores, int64_t ld, const int32_t* tok_pos,
+                       int32_t num_tokens, int32_t max_ctx, int32_t k, int32_t* idx, void* cand,
+                       void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (max_ctx <= kSeg) {
+    const RowArgs a{scores, ld, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
+    hipLaunchKernelGGL(topk_kernel<kDirect>, dim3(num_tokens), dim3(kThreads), 0, st, a);
+  } else {
+    const int nseg = dsa::topk_num_segments(max_ctx);
+    const int kc = (k + 3) & ~3;
+    float* cv = static_cast<float*>(cand);
+    int32_t* cp = reinterpret_cast<int32_t*>(static_cast<char*>(cand) +
+                                             size_t(num_tokens) * nseg * kc * 4);
+    const RowArgs a{scores, ld, tok_pos, max_ctx, k, nseg, kc, cv, cp, idx};
+    hipLaunchKernelGGL(topk_kernel<kSegment>, dim3(nseg, num_tokens), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(num_tokens), dim3(kThreads), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(e));
+  return dsa::ok();
+}
+
+}  // namespace
+
 extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* tok_pos,
                                int32_t num_tokens, int32_t max_ctx, int32_t k, int32_t* idx,
                                void* workspace, size_t workspace_bytes, void* stream) {
@@ -960,24 +992,65 @@ extern "C" dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* t
   s = dsa::check_workspace("dsa_topk", workspace, workspace_bytes,
                            dsa_topk_workspace_bytes(num_tokens, max_ctx, k));
   if (s != DSA_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (max_ctx <= kSeg) {
-    const RowArgs a{scores, ld, tok_pos, max_ctx, k, 1, k, nullptr, nullptr, idx};
-    hipLaunchKernelGGL(topk_kernel<kDirect>, dim3(num_tokens), dim3(kThreads), 0, st, a);
-  } else {
-    const int nseg = dsa::topk_num_segments(max_ctx);
-    const int kc = (k + 3) & ~3;
-    float* cv = static_cast<float*>(workspace);
-    int32_t* cp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                             size_t(num_tokens) * nseg * kc * 4);
-    const RowArgs a{scores, ld, tok_pos, max_ctx, k, nseg, kc, cv, cp, idx};
-    hipLaunchKernelGGL(topk_kernel<kSegment>, dim3(nseg, num_tokens), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(num_tokens), dim3(kThreads), 0, st, a);
-  }
-  hipError_t e = hipGetLastError();
+  return launch_topk("dsa_topk", scores, ld, tok_pos, num_tokens, max_ctx, k, idx, workspace,
+                     stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free top-k: the long-row staging lives in this library-owned
+// device array (one copy per GPU, held until the process ends) instead of a
+// caller workspace.  Host code never uses the array's name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device on its first call and kept.
+static __device__ __align__(256) unsigned char scratch[DSA_TOPK_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess)
-    return dsa::fail(DSA_ERR_HIP, std::string("dsa_topk: launch failed: ") + hipGetErrorString(e));
-  return dsa::ok();
+    return dsa::fail(DSA_ERR_HIP, std::string(who) + ": hipGetDevice failed: " + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return dsa::fail(DSA_ERR_UNSUPPORTED, std::string(who) + ": device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return dsa::fail(DSA_ERR_HIP, std::string(who) + ": hipGetSymbolAddress(scratch) failed: " +
+                                        hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" dsa_status dsa_topk_noalloc(const float* scores, int64_t ld, const int32_t* tok_pos,
+                                       int32_t num_tokens, int32_t max_ctx, int32_t k, int32_t* idx,
+                                       void* stream) {
+  const char* who = "dsa_topk_noalloc";
+  dsa_status s = dsa::check_topk(who, scores, ld, tok_pos, num_tokens, max_ctx, k, idx);
+  if (s != DSA_OK) return s;
+  if (num_tokens == 0) return dsa::ok();
+  const size_t need = dsa_topk_workspace_bytes(num_tokens, max_ctx, k);
+  if (need > DSA_TOPK_SCRATCH_BYTES)
+    return dsa::fail(DSA_ERR_WORKSPACE, std::string(who) + ": the long-row staging needs " +
+                                            std::to_string(need) + " bytes, above the " +
+                                            std::to_string(DSA_TOPK_SCRATCH_BYTES) +
+                                            "-byte library scratch");
+  void* cand = nullptr;
+  if (need > 0) {
+    s = scratch_address(who, &cand);
+    if (s != DSA_OK) return s;
+  }
+  return launch_topk(who, scores, ld, tok_pos, num_tokens, max_ctx, k, idx, cand, stream);
 }
 
 extern "C" size_t dsa_index_topk_workspace_bytes(int32_t num_tokens, int32_t max_ctx, int32_t cap) {

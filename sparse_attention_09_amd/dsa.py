@@ -40,6 +40,7 @@ EXPORTS = [
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
     "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
     "dsa_index_topk_workspace_bytes", "dsa_index_topk", "dsa_dcp_merge", "dsa_combine_shards",
+    "dsa_topk_noalloc",
 ]
 
 
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "dsa_index_scores": (i32, [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, vp, i64, vp]),
             "dsa_topk_workspace_bytes": (sz, [i32, i32, i32]),
             "dsa_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "dsa_topk_noalloc": (i32, [vp, i64, vp, i32, i32, i32, vp, vp]),
             "dsa_plan_partial": (i32, [i32, i32, i32, i32, i32, ctypes.POINTER(PartialPlan)]),
             "dsa_sparse_mla_partial": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32,
                                              i32, vp, vp, vp]),
@@ -262,6 +264,23 @@ def topk(scores: torch.Tensor, tok_pos: torch.Tensor, k: int, max_ctx: int,
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().dsa_topk(_ptr(scores), ld, _ptr(tok_pos), T, max_ctx, k, _ptr(idx),
                           _ptr(workspace), ws_bytes, _stream(dev)))
+    return idx
+
+
+TOPK_SCRATCH_BYTES = 16 << 20   # the library scratch of dsa_topk_noalloc
+
+
+def topk_noalloc(scores: torch.Tensor, tok_pos: torch.Tensor, k: int, max_ctx: int,
+                 idx: torch.Tensor) -> torch.Tensor:
+    """dsa_topk without a workspace: long-row staging in the library's own
+    device scratch (nothing is allocated; idx is caller-provided)."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    T, ld = scores.shape
+    _need(idx, "idx", torch.int32, dev, (T, k))
+    _check(lib().dsa_topk_noalloc(_ptr(scores), ld, _ptr(tok_pos), T, max_ctx, k, _ptr(idx),
+                                  _stream(dev)))
     return idx
 
 
