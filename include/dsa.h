@@ -234,7 +234,7 @@ dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table, int32
 
 /* Dispatch plan of the Partial step [LMSYS-3 and Figure 4].  Host-only.
  *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose
- *   (64, or 32 when width < 1024).
+ *   (32 when num_tokens >= cu_count or width < 1024, else 64).
  *   num_splits: KV splits per token, or 0 = choose from query parallelism
  *   (num_tokens) and cu_count (0 = 256, MI355X): 1 when num_tokens >=
  *   cu_count, else about one workgroup per CU with at least two tiles per

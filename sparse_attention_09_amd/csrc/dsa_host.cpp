@@ -189,17 +189,18 @@ dsa_status dsa_plan_partial(int32_t num_tokens, int32_t width, int32_t kv_tile, 
     return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_plan_partial: kv_tile must be 0, 32, 64 or 128");
   if (num_splits < 0) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_plan_partial: num_splits < 0");
   if (cu_count < 0) return dsa::fail(DSA_ERR_INVALID_ARG, "dsa_plan_partial: cu_count < 0");
-  const int32_t cus = cu_count > 0 ? cu_count : kDefaultCUs;
   // Query parallelism: one workgroup per (token, split), one resident workgroup
   // per CU.  With at least a CU's worth of tokens a single split keeps every CU
-  // busy.  With fewer, splits add workgroups up to one per CU, but each split
-  // keeps at least two tiles: a split's fixed costs (its query rows, its
-  // partial output, Combine's read of it) outweigh the parallelism of a
-  // one-tile split.  Tile 64 cuts loop iterations, softmax updates and
-  // barriers per row; short index rows (under 1024 columns) take tile 32 so
-  // that they still split.
+  // busy, and tile 32 runs the warp-specialized kernel (measured faster than
+  // tile 64 on the 64K verify batch and the 32K prefill chunk).  With fewer
+  // tokens, splits add workgroups up to one per CU, but each split keeps at
+  // least two tiles: a split's fixed costs (its query rows, its partial output,
+  // Combine's read of it) outweigh the parallelism of a one-tile split, so
+  // these batches take tile 64 (half the splits) unless the index row is short
+  // (under 1024 columns), where tile 32 still splits.
+  const int32_t cus = cu_count > 0 ? cu_count : kDefaultCUs;
   int32_t tile = kv_tile;
-  if (tile == 0) tile = width >= 1024 ? 64 : 32;
+  if (tile == 0) tile = (num_tokens >= cus || width < 1024) ? 32 : 64;
   const int32_t iters = (width + tile - 1) / tile;
   int32_t splits = num_splits;
   if (splits == 0) {

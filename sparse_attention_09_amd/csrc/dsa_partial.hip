@@ -52,20 +52,23 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// LDS offset (bf16 units) of 16-byte chunk `chunk` of K-tile row r.  With a
-// 296-dword stride and the chunk index XOR-ed with ((r>>2)^(r>>3))&1, the
-// tile's three access patterns avoid bank conflicts: 16-byte stores by lanes
-// on 8 consecutive rows, 16-byte MFMA-operand reads by lanes on 16 consecutive
-// rows, and 8-byte transpose reads of 4 rows x 32 contiguous bytes.
-__device__ __forceinline__ int k_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-__device__ __forceinline__ int k_chunk_off(int r, int chunk) {
-  return r * kKStride + ((chunk ^ k_swz(r)) << 3);
-}
-// The swizzle only flips bit 0 of the chunk index, so for an even chunk e:
-// chunk e of row r sits at r*stride + 8e + 8*swz(r), chunk e+1 at
-// r*stride + 8e + 8*(1-swz(r)).  Every access below is written as a per-lane
-// base plus compile-time offsets, which keeps address registers out of the
-// tile loop.
+// K-tile layout.  Rows at a 296-dword stride; logical 16-byte chunk x of a
+// row sits at physical chunk k_phys(x) = x ^ bit3(x) (chunks 8..15 of every
+// 16 swap with their neighbour).  Bank behaviour of gfx950's LDS, measured
+// with conflict counters over single access patterns: 16-byte reads are
+// served 32 lanes at a time over 512 bytes of banks (lanes 0..15 with
+// 48..63, then 16..47), 16-byte writes 8 lanes at a time over 128 bytes,
+// 8-byte transpose reads 32 lanes at a time over 256 bytes.  With this
+// stride and chunk map
+//   * MFMA operand reads (16 consecutive rows, one chunk each; the lane
+//     groups read chunks of opposite parity),
+//   * transpose reads (4 rows x 32 bytes per 16 lanes),
+//   * staging writes (8 lanes writing the even chunks 2l of one row: the
+//     bit-3 swap moves half of them to odd chunks)
+// all hit distinct banks.  The map depends only on the chunk index, so every
+// lane-dependent choice is an address, computed once per lane.
+__device__ __forceinline__ constexpr int k_phys(int x) { return x ^ ((x >> 3) & 1); }
+__device__ __forceinline__ int k_chunk_off(int r, int chunk) { return r * kKStride + (k_phys(chunk) << 3); }
 
 // Transposed 4x16-bit read: lane i of each 16-lane group receives element i%4
 // of the 8-byte chunks addressed by lanes 4j + i/4 of its group, j = 0..3.
@@ -188,20 +191,16 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
                  dsa::pack_bf16x2(f[2] * scale, f[3] * scale)};
   }
 
-  // 16 codes -> 16 bf16 = chunks `chunk` (even), `chunk`+1 of row r
+  // 16 codes -> 16 bf16 = logical chunks `chunk` (even) and `chunk`+1 of
+  // row r (physically k_phys(chunk) and k_phys(chunk) ^ 1)
   __device__ __forceinline__ static void put16(uint16_t* k, int r, int chunk, const u32x4& codes,
                                                float scale) {
-    uint32_t b[8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x2 v = dq4(codes[h], scale);
-      b[2 * h] = v[0];
-      b[2 * h + 1] = v[1];
-    }
-    uint16_t* row = k + r * kKStride + 8 * chunk;
-    const int sw = k_swz(r);
-    *reinterpret_cast<u32x4*>(row + 8 * sw) = u32x4{b[0], b[1], b[2], b[3]};
-    *reinterpret_cast<u32x4*>(row + 8 * (1 - sw)) = u32x4{b[4], b[5], b[6], b[7]};
+    const int c0 = k_phys(chunk);
+    uint16_t* row = k + r * kKStride;
+    const u32x2 a0 = dq4(codes[0], scale), a1 = dq4(codes[1], scale);
+    *reinterpret_cast<u32x4*>(row + 8 * c0) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    const u32x2 b0 = dq4(codes[2], scale), b1 = dq4(codes[3], scale);
+    *reinterpret_cast<u32x4*>(row + 8 * (c0 ^ 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
   }
 
   // piece p of row r: rope codes kRP*p..; bf16 chunk 64 + kRP*p/8, and
@@ -218,36 +217,6 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
       const u32x2 lo = dq4(ok ? rcode[0][0] : 0u, sc), hi = dq4(ok ? rcode[0][1] : 0u, sc);
       *reinterpret_cast<u32x4*>(k + k_chunk_off(r, DSA_D_LATENT / 8 + p)) =
           u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-  }
-
-  // The staging of one tile cut into kPieces small steps, to be spread
-  // between MFMAs: steps 0..2kLC-1 store half a latent chunk each (8 codes,
-  // one 16-byte LDS write), step 2kLC the rope piece, then one step per
-  // latent chunk load and one for the rope load.  Every store step runs
-  // before the first load step (a load reuses the registers a store reads).
-  static constexpr int kPieces = 3 * kLC + 2;
-  template <int J>
-  __device__ __forceinline__ void piece(uint16_t* k, int r0, const uint8_t* latent,
-                                        const int32_t* rows, int tid) {
-    static_assert(kRPiece && kLExact, "pieces need the uniform staging layout");
-    if constexpr (J < 2 * kLC) {
-      constexpr int i = J / 2, h = J % 2;
-      const int q = tid + NT * i;
-      const bool ok = (lok >> i) & 1u;
-      const float sc = ok ? lscale[i] : 0.f;
-      const u32x2 lo = dq4(ok ? lcode[i][2 * h] : 0u, sc);
-      const u32x2 hi = dq4(ok ? lcode[i][2 * h + 1] : 0u, sc);
-      const int r = r0 + (q >> 5);
-      // logical chunk 2(q%32) + h sits at physical chunk (2(q%32) + h) ^ swz(r)
-      *reinterpret_cast<u32x4*>(k + r * kKStride + 16 * (q & 31) + 8 * (h ^ k_swz(r))) =
-          u32x4{lo[0], lo[1], hi[0], hi[1]};
-    } else if constexpr (J == 2 * kLC) {
-      store_rope_piece(k, r0, tid);
-    } else if constexpr (J < 3 * kLC + 1) {
-      load_latent(latent, rows, tid, J - 2 * kLC - 1);
-    } else if constexpr (J == 3 * kLC + 1) {
-      load_rope_piece(latent, rows, tid);
     }
   }
 
@@ -418,10 +387,12 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB]
 template <int kKS, int kNB>
 __device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS], f32x4 (&o)[kNB],
                                         int col0, int g, int c) {
-  // lane reads rows 32k2 + 4g + c/4 (+16), whose swizzle bit is fixed per lane
-  const int sw = (g ^ (g >> 1)) & 1;
-  const uint16_t* vbase = k + (4 * g + (c >> 2)) * kKStride + col0 +
-                          8 * ((((c & 3) >> 1)) ^ sw) + 4 * (c & 1);
+  // lane reads rows 32k2 + 4g + c/4 (+16), columns col0 + 16nb + 4(c%4) .. +4:
+  // logical chunk col0/8 + 2nb + (c%4)/2, whose bit 3 (bit 2 of nb when col0
+  // is a multiple of 128) selects the lane base
+  const int vrow = (4 * g + (c >> 2)) * kKStride + col0 + 4 * (c & 1);
+  const uint16_t* vbase0 = k + vrow + 8 * ((c & 3) >> 1);
+  const uint16_t* vbase1 = k + vrow + 8 * (((c & 3) >> 1) ^ 1);
   // two column blocks in flight, their MFMAs alternating
 #pragma unroll
   for (int nb = 0; nb < kNB; nb += 2) {
@@ -430,7 +401,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int k2 = 0; k2 < kKS; ++k2) {
-        const uint16_t* vp = vbase + 32 * k2 * kKStride + 16 * (nb + e);
+        const uint16_t* vp = (((nb + e) >> 2) & 1 ? vbase1 : vbase0) + 32 * k2 * kKStride + 16 * (nb + e);
         const u32x2 lo2 = lds_read_tr16(vp);
         const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
         vb[e][k2] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -545,12 +516,15 @@ __global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
       if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
 
       f32x4 sacc[kMB];
-      const uint16_t* kq = sm.k + c * kKStride + 8 * (g ^ k_swz(c));
+      // logical chunk 4ks + g is physical 4ks + (g ^ bit1(ks))
+      const uint16_t* kq0 = sm.k + c * kKStride + 8 * g;
+      const uint16_t* kq1 = sm.k + c * kKStride + 8 * (g ^ 1);
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DSA_D_QK / 32; ++ks) {
+          const uint16_t* kq = (ks >> 1) & 1 ? kq1 : kq0;
           const u32x4 kf = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
           sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[ks]), sacc[mb]);
         }
@@ -606,8 +580,7 @@ constexpr float kOverflowSum = 4503599627370496.f;   // 2^52
 template <int TILE>
 struct SmemV2 {
   static constexpr int kPStride = TILE + 8;     // bf16 per head in the P buffer
-  static constexpr int kNBuf = TILE == 32 ? 2 : 1;   // K tiles (double buffer at 32 rows)
-  uint16_t k[kNBuf][TILE * kKStride];
+  uint16_t k[TILE * kKStride];
   int32_t rows[kRowChunk];
   float bias[kRowChunk];                        // 0 for a valid row, -inf for a masked one
   f32x4 xs[8][TILE / 32][64];                   // partial S^T sent to the dh partner
@@ -618,7 +591,7 @@ struct SmemV2 {
 
 template <int KV, int TILE, bool kFinal>
 __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
-  static_assert(TILE == 32 || TILE == 64, "tiles of 32 and 64 rows");
+  static_assert(TILE == 64, "tiles of 64 rows (32-row tiles run partial_ws_kernel)");
   __shared__ __attribute__((aligned(16))) SmemV2<TILE> sm;
   constexpr int kPS = SmemV2<TILE>::kPStride;
   constexpr int kOMB = TILE / 32;            // own 16-row blocks per wave
@@ -653,23 +626,19 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   bool overflow = false;
   bool ref_set = false;             // workgroup-uniform: the references are fixed
 
-  // K operand: rows (TILE/2)rh + 16mb + c, dims 288dh + 32ks + 8g
-  const int klane = ((TILE / 2) * rh + c) * kKStride + 8 * ((DSA_D_QK / 16) * dh + (g ^ k_swz(c)));
-  // V transpose read: rows 32k2 + 4g + c/4 (+16), columns 128cq + 16nb
-  const int vsw = (g ^ (g >> 1)) & 1;
-  const int vlane = (4 * g + (c >> 2)) * kKStride + (DSA_D_LATENT / 4) * cq +
-                    8 * (((c & 3) >> 1) ^ vsw) + 4 * (c & 1);
+  // K operand: rows (TILE/2)rh + 16mb + c, dims 288dh + 32ks + 8g = logical
+  // chunk 36dh + 4ks + g, physical 36dh + 4ks + (g ^ bit3(36dh + 4ks))
+  const int krow = ((TILE / 2) * rh + c) * kKStride + 8 * (DSA_D_QK / 16) * dh;
+  const int klane0 = krow + 8 * g, klane1 = krow + 8 * (g ^ 1);
+  const int kb = (DSA_D_QK / 64) * dh;       // bit3(36dh + 4ks) = bit1(9dh + ks)
+  // V transpose read: rows 32k2 + 4g + c/4 (+16), columns 128cq + 16nb: logical
+  // chunk 16cq + 2nb + (c%4)/2, whose bit 3 (bit 2 of nb) selects the base
+  const int vrow = (4 * g + (c >> 2)) * kKStride + (DSA_D_LATENT / 4) * cq + 4 * (c & 1);
+  const int vlane0 = vrow + 8 * ((c & 3) >> 1), vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
   // P: written at head 32hp + 16dh + c, read as the A operand of head 32hp + 16hb + c
   uint16_t* pw = sm.p + (32 * hp + 16 * dh + c) * kPS;
 
-  // stage(integral_constant<int, J>) is called after the QK MFMAs of k-step J
-  // (J = 0..kQS-1): work that needs no result of this tile, i.e. the next
-  // tile's staging with a double buffer.  For FP8 double buffering the steps
-  // are pinned between the MFMAs (a scheduling barrier after each k-step, the
-  // next K fragment read one step ahead), so the dequantization VALU work
-  // overlaps the matrix pipe instead of following it.
-  constexpr bool kPipeQK = SmemV2<TILE>::kNBuf == 2 && KV == DSA_KV_FP8_E4M3_S64 && kOMB == 1;
-  auto compute_tile = [&](int it, const uint16_t* kt, auto&& stage) {
+  auto compute_tile = [&](int it, const uint16_t* kt) {
     // S^T over this wave's rows and half of the dims, starting at the row bias
     f32x4 sacc[kOMB][2];
 #pragma unroll
@@ -679,34 +648,19 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       sacc[mb][0] = b;
       sacc[mb][1] = b;
     }
-    const uint16_t* kq = kt + klane;
-    if constexpr (kPipeQK) {
-      u32x4 kn = *reinterpret_cast<const u32x4*>(kq);
-      dsa::static_for<kQS>([&](auto KS) {
-        constexpr int ks = decltype(KS)::value;
-        const u32x4 kf = kn;
-        if constexpr (ks + 1 < kQS) kn = *reinterpret_cast<const u32x4*>(kq + 32 * (ks + 1));
+#pragma unroll
+    for (int ks = 0; ks < kQS; ++ks) {
+      const uint16_t* kq = kt + (((kb + ks) >> 1) & 1 ? klane1 : klane0);
+      u32x4 kf[kOMB];
+#pragma unroll
+      for (int mb = 0; mb < kOMB; ++mb)
+        kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
+#pragma unroll
+      for (int mb = 0; mb < kOMB; ++mb)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          sacc[0][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[hb][ks]), sacc[0][hb]);
-        stage(KS);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kQS; ++ks) {
-        u32x4 kf[kOMB];
-#pragma unroll
-        for (int mb = 0; mb < kOMB; ++mb)
-          kf[mb] = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
-#pragma unroll
-        for (int mb = 0; mb < kOMB; ++mb)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
-                                             sacc[mb][hb]);
-      }
-      dsa::static_for<kQS>(stage);
+          sacc[mb][hb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf[mb]), dsa::as_bf16x8(qf[hb][ks]),
+                                           sacc[mb][hb]);
     }
     // keep head block dh, send head block 1-dh to the partner (wave ^ 2)
     f32x4 sv[kOMB];
@@ -764,12 +718,11 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
 #pragma unroll
       for (int k2 = 0; k2 < kKS; ++k2)
         pa[hb][k2] = *reinterpret_cast<const u32x4*>(sm.p + (32 * hp + 16 * hb + c) * kPS + 32 * k2 + 8 * g);
-    const uint16_t* vb0 = kt + vlane;
 #pragma unroll
     for (int k2 = 0; k2 < kKS; ++k2)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const uint16_t* vp = vb0 + 32 * k2 * kKStride + 16 * nb;
+        const uint16_t* vp = kt + ((nb >> 2) & 1 ? vlane1 : vlane0) + 32 * k2 * kKStride + 16 * nb;
         const u32x2 lo2 = lds_read_tr16(vp);
         const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
         const u32x4 vb = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -808,40 +761,16 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       const int ntile = (sm.last + TILE) / TILE;
       if (ntile == 0) continue;
       st.load(a.latent, sm.rows, tid);
-      st.store(sm.k[0], 0, tid);
-      if constexpr (SmemV2<TILE>::kNBuf == 2) {
-        // tile it+1 waits in registers; during tile it it goes to the other
-        // buffer (free since the last barrier) and tile it+2 is fetched.  Both
-        // run unconditionally (row indices clamped into the chunk): past the
-        // last tile they refill the idle buffer with data nobody reads.
-        st.load(a.latent, sm.rows + min(1, ntile - 1) * TILE, tid);
+      st.store(sm.k, 0, tid);
+      __syncthreads();
+      for (int it = 0; it < ntile; ++it) {
+        const bool more = it + 1 < ntile;
+        if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
+        compute_tile(it, sm.k);
         __syncthreads();
-        for (int it = 0; it < ntile; ++it) {
-          uint16_t* knext = sm.k[(it + 1) & 1];
-          const int32_t* rows2 = sm.rows + min(it + 2, ntile - 1) * TILE;
-          compute_tile(it, sm.k[it & 1], [&](auto J) {
-            constexpr int j = decltype(J)::value;
-            if constexpr (kPipeQK) {
-              static_assert(decltype(st)::kPieces <= kQS, "staging steps fit the k-steps");
-              st.template piece<j>(knext, 0, a.latent, rows2, tid);
-            } else if constexpr (j == kQS - 1) {
-              st.store(knext, 0, tid);
-              st.load(a.latent, rows2, tid);
-            }
-          });
+        if (more) {
+          st.store(sm.k, 0, tid);
           __syncthreads();
-        }
-      } else {
-        __syncthreads();
-        for (int it = 0; it < ntile; ++it) {
-          const bool more = it + 1 < ntile;
-          if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
-          compute_tile(it, sm.k[0], [](auto) {});
-          __syncthreads();
-          if (more) {
-            st.store(sm.k[0], 0, tid);
-            __syncthreads();
-          }
         }
       }
     }
@@ -872,10 +801,286 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialized kernel, tiles of 32 rows: 8 waves, one workgroup per
+// (token, split), two roles with one wave of each on every SIMD.
+//   * Score waves 0..3: wave w computes S^T for heads 16w..+16 over all 576
+//     dims and the tile's 32 rows (the Q of its heads stays in registers, so
+//     no partial sums are exchanged between waves), runs the online softmax
+//     with a running per-head max (O is rescaled only when a head's max grows
+//     by more than 2^8) and writes P and the per-head rescale factor to LDS.
+//   * Value waves 4..7: wave 4+q accumulates O for all 64 heads on output
+//     columns 128q..+128; each transposed V fragment read feeds four head
+//     blocks.
+// The roles run one tile apart: in iteration j the score waves work on tile
+// j while the value waves run PV of tile j-1, so on each SIMD one wave's
+// MFMAs can overlap the other wave's softmax and staging work instead of
+// every wave passing through the same phase between barriers.  K tiles are a
+// ring of three bf16 buffers (score waves read tile j, value waves tile j-1,
+// tile j+1 is staged into the third) and P a ring of two: one barrier per
+// tile.  The score waves also stage (the value waves hold the 128-register O
+// accumulator and have no room): the selected rows are gathered kD tiles ahead
+// into their registers (3 for FP8 rows, 1 for the wider BF16 rows),
+// dequantized and stored to LDS once, in small steps placed between the QK
+// MFMAs so that the VALU and LDS work runs beside the matrix pipe.
+constexpr int kTileWS = 32;
+constexpr int kWSKLook = 2;                 // k-steps ahead the score waves read K fragments
+constexpr int kPStrideWS = kTileWS;         // bf16 per head in a P buffer (64 bytes)
+
+// 16-byte chunk of a P row: logical chunk g (PV operand positions 8g..8g+7)
+// of head h sits at g ^ p_swz(h).  With this XOR the score waves' 16-byte
+// writes (8 lanes on 8 heads) and the value waves' 16-byte operand reads (16
+// heads x 4 chunks) are both free of bank conflicts.
+__device__ __forceinline__ int p_swz(int h) { return (((h >> 1) ^ (h >> 3)) & 1) | (((h >> 2) & 1) << 1); }
+
+struct SmemWS {
+  uint16_t k[3][kTileWS * kKStride];          // bf16 K tiles (ring of three)
+  uint16_t p[2][DSA_HEADS * kPStrideWS];      // P of a tile in the PV operand's row order
+  float alpha[2][DSA_HEADS];                  // O *= alpha before PV of that tile
+  int32_t rows[kRowChunk];
+  float bias[kRowChunk];                      // 0 for a valid row, -inf for a masked one
+  float fin_l[DSA_HEADS];
+  int last;
+};
+
+template <int KV>
+constexpr int ws_depth() { return KV == DSA_KV_FP8_E4M3_S64 ? 3 : 1; }
+
+
+// The tile pipeline shared by both roles, so that both execute exactly the
+// same barriers: per row chunk the rows are resolved, tiles 0..kD-1 are
+// fetched and tile 0 staged; iteration j = 0, 1, ... (at least through ntile,
+// in whole groups of three) calls work(j, ntile, P) (P = j % 3 at compile
+// time; work contains no barrier and does no role work past ntile), stages
+// tile j+1 into K buffer (j+1) % 3, fetches tile j+1+kD and waits at the
+// barrier.  Every thread stages, after its role work: with the staging
+// spread between the score waves' MFMAs, or done by the score waves alone,
+// the kernel measured slower.  Loads and stores run unconditionally (row
+// indices clamped to the chunk's last tile): past the last tile they refill
+// a buffer nobody reads.
+template <int KV, class Work>
+__device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, int t, int req,
+                                            int pos, int c0, int c1, int tid, Work&& work) {
+  constexpr int TILE = kTileWS;
+  constexpr int kD = ws_depth<KV>();
+  Stage<KV, TILE, kThreadsV2> st[kD];
+  for (int cc = c0; cc < c1; cc += kRowChunk) {
+    const int cend = min(c1, cc + kRowChunk);
+    __syncthreads();                            // every thread has read the last chunk's state
+    if (tid == 0) sm.last = -1;
+    __syncthreads();
+    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
+    __syncthreads();
+    const int ntile = (sm.last + TILE) / TILE;
+    if (ntile == 0) continue;
+    auto tile_rows = [&](int i) { return sm.rows + min(i, ntile - 1) * TILE; };
+    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), tid); });
+    st[0].store(sm.k[0], 0, tid);
+    st[0].load(a.latent, tile_rows(kD), tid);
+    __syncthreads();
+    // Whole groups of three iterations, every one staging and fetching: the
+    // fetches then form one straight-line stream whose in-order completion
+    // counts the compiler can track (a conditional iteration makes it wait
+    // for every load in flight).  work() skips iterations past ntile.
+    for (int j0 = 0; j0 <= ntile; j0 += 3) {
+      dsa::static_for<3>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        const int j = j0 + p;
+        constexpr int si = (p + 1) % kD;
+        work(j, ntile, P);
+        st[si].store(sm.k[(p + 1) % 3], 0, tid);
+        st[si].load(a.latent, tile_rows(j + 1 + kD), tid);
+        __syncthreads();
+      });
+    }
+  }
+}
+
+template <int KV, bool kFinal>
+__global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(16))) SmemWS sm;
+  constexpr int TILE = kTileWS;
+  constexpr int kQS = DSA_D_QK / 32;           // 18 QK k-steps
+  constexpr int kNB = DSA_D_LATENT / 64;       // 8 column blocks of a value wave
+
+  const int t = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int c0 = s * a.cols_per_split;
+  const int c1 = min(a.width, c0 + a.cols_per_split);
+  const int req = request_of(a, t);
+  const int pos = a.tok_pos[t];
+  const int64_t ts = int64_t(t) * a.splits + s;
+
+  if (wave < 4) {
+    // ---- score wave: heads 16*wave + c (lane column c)
+    const int head = 16 * wave + c;
+    u32x4 qf[kQS];   // Q of heads 16*wave..+16, dims 32ks + 8g .. +8 (MFMA B operand)
+    {
+      const u32x4* qsrc = reinterpret_cast<const u32x4*>(a.q + (int64_t(t) * DSA_HEADS + head) * DSA_D_QK);
+#pragma unroll
+      for (int ks = 0; ks < kQS; ++ks) qf[ks] = qsrc[ks * 4 + g];
+    }
+    float m_run = kNegInf, l_run = 0.f;
+    // K operand: rows 16mb + c, dims 32ks + 8g = logical chunk 4ks + g, physical
+    // 4ks + (g ^ bit1(ks))
+    const int klane0 = c * kKStride + 8 * g;
+    const int klane1 = c * kKStride + 8 * (g ^ 1);
+    ws_pipeline<KV>(a, sm, t, req, pos, c0, c1, tid, [&](int j, int ntile, auto P) {
+      constexpr int p = decltype(P)::value;
+      if (j < ntile) {
+        const uint16_t* kq0 = sm.k[p] + klane0;
+        const uint16_t* kq1 = sm.k[p] + klane1;
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          sacc[mb] = *reinterpret_cast<const f32x4*>(sm.bias + j * TILE + 16 * mb + 4 * g);
+        // K fragments of k-step ks (rows 16mb + c) in a ring of kWSKLook + 1
+        auto kread = [&](int ks, int mb) {
+          const uint16_t* kq = (ks >> 1) & 1 ? kq1 : kq0;
+          return *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
+        };
+        u32x4 kr[kWSKLook + 1][2];
+        dsa::static_for<kWSKLook>([&](auto L) {
+          constexpr int l = decltype(L)::value;
+          kr[l][0] = kread(l, 0);
+          kr[l][1] = kread(l, 1);
+        });
+        dsa::static_for<kQS>([&](auto KS) {
+          constexpr int ks = decltype(KS)::value;
+          if constexpr (ks + kWSKLook < kQS) {
+            kr[(ks + kWSKLook) % (kWSKLook + 1)][0] = kread(ks + kWSKLook, 0);
+            kr[(ks + kWSKLook) % (kWSKLook + 1)][1] = kread(ks + kWSKLook, 1);
+          }
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kr[ks % (kWSKLook + 1)][mb]),
+                                         dsa::as_bf16x8(qf[ks]), sacc[mb]);
+        });
+        // tile max of the head (log2 units; -inf when every row is masked)
+        float tmax = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) tmax = fmaxf(tmax, sacc[mb][jj]);
+        tmax = dsa::rows4_max(tmax) * a.scale_log2;
+        float alpha = 1.f;
+        if (tmax > m_run + kRescaleThreshold) {
+          if (m_run != kNegInf) alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+          l_run *= alpha;
+          m_run = tmax;
+        }
+        // masked rows: -inf * scale - m = -inf, exp2 gives 0; while no row has
+        // been valid m is -inf and every row so far is masked
+        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+        // rows 16mb + 4g + jj -> PV operand position 8g + 4mb + jj: this lane's
+        // eight values are logical chunk g of the head's P row
+        float psum = 0.f;
+        uint32_t pk[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          float pr[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            pr[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][jj], a.scale_log2, neg_m));
+            psum += pr[jj];
+          }
+          pk[2 * mb] = dsa::pack_bf16x2(pr[0], pr[1]);
+          pk[2 * mb + 1] = dsa::pack_bf16x2(pr[2], pr[3]);
+        }
+        *reinterpret_cast<u32x4*>(sm.p[j & 1] + head * kPStrideWS + 8 * (g ^ p_swz(c))) =
+            u32x4{pk[0], pk[1], pk[2], pk[3]};
+        l_run += dsa::rows4_sum(psum);
+        if (g == 0) sm.alpha[j & 1][head] = alpha;
+      }
+    });
+    if (g == 0) {
+      sm.fin_l[head] = l_run;
+      put_lse<kFinal>(a, ts, head, l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : kNegInf);
+    }
+    __syncthreads();
+  } else {
+    // ---- value wave: all 64 heads, output columns 128q..+128
+    const int q = wave - 4;
+    f32x4 o[4][kNB];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // V transpose read: rows 4g + c/4 (+16), columns 128q + 16nb
+    // logical chunk 16q + 2nb + (c%4)/2, bit 3 = bit 2 of nb selects the base
+    const int vrow = (4 * g + (c >> 2)) * kKStride + (DSA_D_LATENT / 4) * q + 4 * (c & 1);
+    const int vlane0 = vrow + 8 * ((c & 3) >> 1);
+    const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
+    ws_pipeline<KV>(a, sm, t, req, pos, c0, c1, tid, [&](int j, int ntile, auto P) {
+      constexpr int p = decltype(P)::value;
+      if (j >= 1 && j <= ntile) {
+        const int jp = j - 1;   // PV of the previous tile, in K buffer (p + 2) % 3
+        // O *= alpha of the heads this lane holds (rows 4g + jj of each head block)
+        f32x4 al[4];
+        bool rescale = false;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          al[hb] = *reinterpret_cast<const f32x4*>(sm.alpha[jp & 1] + 16 * hb + 4 * g);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[hb][jj] != 1.f;
+        }
+        if (__any(rescale)) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[hb][jj];
+        }
+        const uint16_t* pb = sm.p[jp & 1];
+        u32x4 pa[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          pa[hb] = *reinterpret_cast<const u32x4*>(pb + (16 * hb + c) * kPStrideWS + 8 * (g ^ p_swz(c)));
+        // V fragments read one column block ahead; one staging step of the
+        // next tile after each block's four MFMAs
+        const uint16_t* vt = sm.k[(p + 2) % 3];
+        auto vread = [&](int nb) {
+          const uint16_t* vp = vt + ((nb >> 2) & 1 ? vlane1 : vlane0) + 16 * nb;
+          const u32x2 lo2 = lds_read_tr16(vp);
+          const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
+          return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+        u32x4 vb = vread(0);
+        dsa::static_for<kNB>([&](auto NB) {
+          constexpr int nb = decltype(NB)::value;
+          u32x4 vn;
+          if constexpr (nb + 1 < kNB) vn = vread(nb + 1);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+            o[hb][nb] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[hb]), dsa::as_bf16x8(vb), o[hb][nb]);
+          if constexpr (nb + 1 < kNB) vb = vn;
+        });
+      }
+    });
+    __syncthreads();   // the score waves have written each head's sum
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int hh = 16 * hb + 4 * g + jj;
+        const float l = sm.fin_l[hh];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          put_out<kFinal>(a, ts, hh, (DSA_D_LATENT / 4) * q + 16 * nb + c, o[hb][nb][jj] * inv);
+      }
+  }
+}
+
 template <int KV, int TILE, bool kFinal>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
   if constexpr (TILE == kTile4)
     hipLaunchKernelGGL((partial4_kernel<KV, kFinal>), dim3(T, S), dim3(kThreads4), 0, st, a);
+  else if constexpr (TILE == kTileWS)
+    hipLaunchKernelGGL((partial_ws_kernel<KV, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   else
     hipLaunchKernelGGL((partial_v2_kernel<KV, TILE, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   return hipGetLastError();

@@ -168,7 +168,7 @@ def test_plan_dispatch_uses_query_parallelism():
     # enough query tokens for every CU: one split (no combine work beyond a copy)
     p = dsa.plan_partial(1024, 2048, 0, 0, 256)
     assert p.splits == 1
-    assert p.tile == 64
+    assert p.tile == 32
     # few tokens: splits supply the parallelism up to one workgroup per CU,
     # with at least two tiles per split
     p = dsa.plan_partial(8, 2048, 0, 0, 256)
