@@ -10,6 +10,11 @@ each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --summarize-stats KERNEL_STATS_CSV COMMAND...      (rocprofv3 summary text)
   python bench.py --summarize-pmc FETCH_CSV WRITE_CSV WORKLOAD CMD... (traffic JSON)
+  python bench.py --summarize-mfma COUNTER_CSV WORKLOAD CMD...        (MFMA-use JSON)
+
+With no flags the line also carries the 32K-token prefill chunk (Partial
+against the bf16 MFMA peak), the shared-prefix batch at KV tiles 32 / 64 /
+128, and the box's measured copy bandwidth and bf16 GEMM rate.
 """
 
 from __future__ import annotations
@@ -164,6 +169,8 @@ def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
     except OSError:
         pass
     return {"value": done / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "parallelism": f"one process, tokens one after another; numpy's BLAS uses {threads} "
+                           f"thread(s) inside each matrix product",
             "sample": f"{done} query tokens of {s.name} (requests {reqs[0]}..{reqs[-1]}), "
                       f"full per-token path (indexer over the whole context, top-k, attention, "
                       f"combine) in float64 numpy; {dt:.1f} s",
@@ -277,6 +284,58 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands: list)
     return out
 
 
+def summarize_mfma(csv_path: str, workload: str, commands: list) -> dict:
+    """Matrix-core use of each path kernel from a rocprofv3 counter run with
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 FLOPs), SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over SIMDs), GRBM_GUI_ACTIVE (summed over the 8 XCDs) and,
+    optionally, the derived MfmaUtil (per cent).  Per launch: the counted
+    bf16 MFMA TFLOP/s over the dispatch's own duration, and the share of SIMD
+    cycles the matrix pipe was busy."""
+    import csv
+    import statistics
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = _kernel_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    simds = 256 * 4
+    out = {"workload": workload, "commands": commands,
+           "counters": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs; SQ_VALU_MFMA_BUSY_CYCLES / "
+                       "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); MfmaUtil as rocprofv3 derives it",
+           "kernels": {}}
+    for k, ds in per.items():
+        rows = list(ds.values())
+        e = {"dispatches": len(rows), "source_sha": source_sha(k)}
+        mops = [r["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for r in rows if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in r]
+        ns = [r["_ns"] for r in rows if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in r]
+        if mops:
+            e["mfma_tflops_counted"] = round(statistics.median(
+                m * 512 / (t * 1e-9) / 1e12 for m, t in zip(mops, ns)), 1)
+            e["mfma_flops_counted"] = int(statistics.median(m * 512 for m in mops))
+        busy = [r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] / 8 * simds)
+                for r in rows if "SQ_VALU_MFMA_BUSY_CYCLES" in r and r.get("GRBM_GUI_ACTIVE")]
+        if busy:
+            e["busy_cycles_frac"] = round(statistics.median(busy), 4)
+        util = [r["MfmaUtil"] for r in rows if "MfmaUtil" in r]
+        if util:
+            e["mfma_util"] = round(statistics.median(util) / 100.0, 4)
+        elif busy:
+            e["mfma_util"] = e["busy_cycles_frac"]
+        out["kernels"][k] = e
+    parts = [k for k in FUSED_SELECT if k in out["kernels"]]
+    if parts:
+        # the fused selection: its five launches together
+        fl = sum(out["kernels"][k].get("mfma_flops_counted", 0) for k in parts)
+        out["kernels"]["index_topk"] = {"parts": parts, "mfma_flops_counted": fl,
+                                        "mfma_util": out["kernels"].get("index_emit", {}).get("mfma_util"),
+                                        "note": "mfma_util of the emit pass, which does all but 1/32 of the MFMA work",
+                                        "source_sha": source_sha("index_topk")}
+    return out
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
@@ -291,6 +350,197 @@ def measured_traffic(workload: str, kernel: str):
     return d["traffic_bytes"]
 
 
+FLUSH_BYTES = 1 << 30           # read between timed steps: evicts L2 and the 256 MB MALL
+
+
+def make_flush(dev):
+    """A read of 1 GiB (a sum): it replaces the caches' contents with clean
+    lines, so the next step starts cold without paying for write-backs (a
+    1 GiB fill measured ~60 us of dirty-line write-back in the next kernel)."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush(i):
+        torch.sum(buf, dim=0, out=acc)
+    return flush
+
+
+def time_steps(calls, names, steps, stream, flush=None):
+    """`steps` steps of the calls in order on `stream`.  Before each step the
+    cache-flush write runs, outside the events; each call is bracketed by
+    events.  Returns the per-step times (ms) and each call's mean duration
+    (us) over the same steps."""
+    import statistics
+    n = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if flush is not None:
+            flush(i)
+        ev[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [ev[i][0].elapsed_time(ev[i][n]) for i in range(steps)]
+    per_us = {nm: 1000.0 * statistics.mean(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps))
+              for j, nm in enumerate(names)}
+    return step_ms, per_us
+
+
+def measure_peaks(dev, reps=10):
+    """The box's own denominators: a 1 GiB device copy (GB/s, read + write)
+    and an 8192^3 bf16 GEMM through torch (TFLOP/s, dense MFMA)."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * 4 * a.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(1)
+    x = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    y = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    z = x @ y
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        z = torch.matmul(x, y, out=z)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"copy_gbps": round(copy_gbps, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+            "copy": "1 GiB device-to-device copy (bytes read + written)",
+            "gemm": "8192 x 8192 x 8192 bf16 torch.matmul"}
+
+
+def setup_path(dsa, synth, name, dev, cus, tile=0, splits=0, select="auto", seed=0):
+    spec = synth.spec(name)
+    print(f"[bench] generating {spec.name} seed={seed}", file=sys.stderr, flush=True)
+    wl = synth.generate(spec, seed=seed, device=dev)
+    torch.cuda.synchronize()
+    pool = dsa.Pool(wl.pool, wl.num_pages, spec.kv_dtype)
+    path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx, spec.k,
+                       kv_tile=tile, num_splits=splits, sm_scale=spec.sm_scale, cu_count=cus,
+                       select=select)
+    # one step = these calls in order (what DsaPath.step runs)
+    if path.fused_topk:
+        names = ["index_topk"]
+        calls = [lambda: path.index_topk(wl.q_idx, wl.w)]
+    else:
+        names = ["index_scores", "topk"]
+        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk]
+    if path.fused:
+        names += ["partial"]
+        calls += [lambda: path.attend(wl.q)]
+    else:
+        names += ["partial", "combine"]
+        calls += [lambda: path.partial(wl.q), path.combine]
+    return spec, wl, pool, path, names, calls
+
+
+def mfma_counters(workload: str, kernel: str):
+    """MFMA utilisation of a kernel from the committed rocprofv3 counter
+    summary (profiles/<workload>_mfma.json), or None when absent or taken on
+    other kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{workload}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not d or d.get("source_sha") != source_sha(kernel):
+        return None
+    return {k: d[k] for k in ("mfma_util", "mfma_tflops_counted", "busy_cycles_frac") if k in d}
+
+
+def bench_prefill(dsa, synth, dev, cus, flush, peaks, steps=5, warmup=2):
+    """The 32K-token prefill chunk: Partial against the bf16 MFMA peak."""
+    import statistics
+    spec, wl, pool, path, names, calls = setup_path(dsa, synth, "prefill_fp8_32k", dev, cus)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        path.step(wl.q_idx, wl.w, wl.q)
+    step_ms, per_us = time_steps(calls, names, steps, stream, flush)
+    fl = flops(spec)
+    kern = {}
+    for n in names:
+        d = {"avg_us": round(per_us[n], 1)}
+        if n in fl:
+            tf = fl[n] / (per_us[n] * 1e-6) / 1e12
+            d.update({"tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        kern[n] = d
+    med = statistics.median(step_ms)
+    tf = kern["partial"]["tflops"]
+    out = {"workload": spec.name, "query_tokens": spec.num_tokens, "steps": steps,
+           "ms_per_step": round(med, 3), "query_tokens_per_s": round(spec.num_tokens / (med * 1e-3), 1),
+           "kv_tile": path.plan.tile, "kernels": kern,
+           "roofline": {"kernel": "partial", "bound": "mfma", "achieved": tf,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                        "measured_peak": peaks["bf16_gemm_tflops"],
+                        "frac_of_measured": round(tf / peaks["bf16_gemm_tflops"], 4),
+                        "flops_per_launch": int(fl["partial"]),
+                        "counters": mfma_counters(spec.name, "partial")},
+           "fallback_tokens": path.fallback_count()}
+    pool.close()
+    del wl, path, pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=10, warmup=3, tiles=(32, 64, 128)):
+    """132 requests sharing a 63,488-token prefix: Partial at KV tiles 32, 64
+    and 128 (one split each) on the same selected indices.  Logical bytes are
+    the rows as gathered; unique bytes count each physical row once (the
+    shared rows come from the caches, so HBM sees about the unique bytes)."""
+    import statistics
+    spec, wl, pool, path, _, _ = setup_path(dsa, synth, "shared_prefix_fp8", dev, cus)
+    stream = torch.cuda.current_stream(dev)
+    path.select(wl.q_idx, wl.w)
+    torch.cuda.synchronize()
+    T, k = spec.num_tokens, spec.k
+    idx = path.idx.to(torch.int64)
+    req = wl.tok_req.to(torch.int64)[:, None].expand_as(idx)
+    phys = wl.page_table.to(torch.int64)[req, torch.clamp(idx, min=0) // 64] * 64 + idx % 64
+    uniq_rows = int(torch.unique(phys[idx >= 0]).numel())
+    lay = dsa.pool_layout(spec.kv_dtype, 1)
+    fixed = T * k * 4 + T * 64 * 576 * 2 + T * 64 * (512 * 2 + 4)     # idx, q, output
+    logical = fixed + T * k * lay.latent_row_bytes
+    unique = fixed + uniq_rows * lay.latent_row_bytes
+    res = {}
+    for tile in tiles:
+        out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+
+        def call(tile=tile, out=out, lse=lse):
+            dsa.sparse_mla(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q, path.idx,
+                           spec.sm_scale, tile, out, lse)
+        for _ in range(warmup):
+            call()
+        step_ms, _ = time_steps([call], ["partial"], steps, stream, flush)
+        us = 1000.0 * statistics.median(step_ms)
+        res[str(tile)] = {"avg_us": round(us, 1),
+                          "logical_gbps": round(logical / (us * 1e-6) / 1e9, 1),
+                          "unique_gbps": round(unique / (us * 1e-6) / 1e9, 1)}
+    out = {"workload": spec.name, "query_tokens": T, "splits": 1, "partial_by_tile": res,
+           "logical_bytes": int(logical), "unique_bytes": int(unique), "unique_rows": uniq_rows,
+           "tile128_speedup_over_tile32": round(res["32"]["avg_us"] / res["128"]["avg_us"], 3),
+           "note": "one split per token; the pages report Partial + Combine at KV tile 128 about "
+                   "1.12x faster than at tile 32 on H200 (context, other hardware)"}
+    pool.close()
+    del wl, path, pool
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
         print(summarize_stats(sys.argv[2], " ".join(sys.argv[3:])), end="")
@@ -298,6 +548,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         fetch_csv, write_csv, workload = sys.argv[2:5]
         print(json.dumps(summarize_pmc(fetch_csv, write_csv, workload, sys.argv[5:]), indent=1))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        csv_path, workload = sys.argv[2:4]
+        print(json.dumps(summarize_mfma(csv_path, workload, sys.argv[4:]), indent=1))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +568,10 @@ def main():
     ap.add_argument("--no-dcp", action="store_true", help="skip the DCP shard-layout timing")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing a HIP graph replay of the step")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time back-to-back steps without the cache flush between them")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the prefill and shared-prefix entries and the measured peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
                          "(reference dispatch for HBM byte counters)")
@@ -325,35 +583,17 @@ def main():
 
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from sparse_attention_09_amd import dsa, synth
+    import statistics
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    spec = synth.spec(args.workload)
-    print(f"[bench] generating {spec.name} seed={args.seed}", file=sys.stderr, flush=True)
-    wl = synth.generate(spec, seed=args.seed, device=dev)
-    torch.cuda.synchronize()
-    pool = dsa.Pool(wl.pool, wl.num_pages, spec.kv_dtype)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    path = dsa.DsaPath(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.max_q, wl.max_ctx, spec.k,
-                       kv_tile=args.tile, num_splits=args.splits, sm_scale=spec.sm_scale,
-                       cu_count=cus, select=args.select)
+    spec, wl, pool, path, names, calls = setup_path(dsa, synth, args.workload, dev, cus, args.tile,
+                                                    args.splits, args.select, args.seed)
     plan = path.plan
     print(f"[bench] plan tile={plan.tile} splits={plan.splits} cus={cus} "
           f"selection={'fused' if path.fused_topk else 'scores+topk'}", file=sys.stderr, flush=True)
-
-    # one step = these calls in order (what DsaPath.step runs)
-    if path.fused_topk:
-        names = ["index_topk"]
-        calls = [lambda: path.index_topk(wl.q_idx, wl.w)]
-    else:
-        names = ["index_scores", "topk"]
-        calls = [lambda: path.index_scores(wl.q_idx, wl.w), path.topk]
-    if path.fused:
-        names += ["partial"]
-        calls += [lambda: path.attend(wl.q)]
-    else:
-        names += ["partial", "combine"]
-        calls += [lambda: path.partial(wl.q), path.combine]
+    flush = None if args.no_flush else make_flush(dev)
 
     def step():
         path.step(wl.q_idx, wl.w, wl.q)
@@ -362,30 +602,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, with an event recorded on the working stream
-    # before the first call and after every call, so the step time and each
-    # kernel's average launch duration come from the same K steps.
+    # Timed region: K steps, each preceded by the cache flush (outside the
+    # events), with an event on the working stream before the first call and
+    # after every call: the step time and each kernel's average launch
+    # duration come from the same K steps.
     stream = torch.cuda.current_stream(dev)
-    n = len(calls)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        for j, c in enumerate(calls):
-            c()
-            evs[i * n + j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_total = evs[0].elapsed_time(evs[-1])
-    ms_step = ms_total / args.steps
-    acc = {nm: 0.0 for nm in names}
-    for i in range(args.steps):
-        for j, nm in enumerate(names):
-            acc[nm] += evs[i * n + j].elapsed_time(evs[i * n + j + 1])
-    per_us = {nm: 1000.0 * acc[nm] / args.steps for nm in names}
-    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    step_ms, per_us = time_steps(calls, names, args.steps, stream, flush)
+    ms_step = statistics.median(step_ms)
+    print(f"[bench] {args.steps} steps, median {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # the same K steps without the markers between calls (a check that the
-    # markers cost nothing measurable)
+    # the same K steps back to back, no flush and no markers between calls
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -415,18 +641,9 @@ def main():
         path.index_scores(wl.q_idx, wl.w)
         path.topk()
         torch.cuda.synchronize()
-        u = {"index_scores": 0.0, "topk": 0.0}
-        for _ in range(args.steps):
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            evs[0].record(stream)
-            path.index_scores(wl.q_idx, wl.w)
-            evs[1].record(stream)
-            path.topk()
-            evs[2].record(stream)
-            torch.cuda.synchronize()
-            u["index_scores"] += evs[0].elapsed_time(evs[1])
-            u["topk"] += evs[1].elapsed_time(evs[2])
-        unfused = {n: round(1000.0 * v / args.steps, 3) for n, v in u.items()}
+        _, u = time_steps([lambda: path.index_scores(wl.q_idx, wl.w), path.topk],
+                          ["index_scores", "topk"], args.steps, stream, flush)
+        unfused = {n: round(v, 3) for n, v in u.items()}
         path.scores = path.workspace = None
         torch.cuda.empty_cache()
 
@@ -445,12 +662,21 @@ def main():
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
     T = spec.num_tokens
     value = T / (ms_step * 1e-3)
+    peaks = None if args.no_extra else measure_peaks(dev)
+    # the decode batches are bound by HBM: the roof of the dominant kernel is
+    # its algorithmic bytes over the HBM peak (also given against the box's
+    # measured copy bandwidth)
     roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(kernels[dom]["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(spec.name, dom),
             "alg_bytes_per_launch": int(byts[dom]), "avg_us": kernels[dom]["avg_us"]}
+    if peaks:
+        roof["measured_peak"] = peaks["copy_gbps"]
+        roof["frac_of_measured"] = round(kernels[dom]["gbps"] / peaks["copy_gbps"], 4)
     for n in names:
         kernels[n]["traffic_bytes"] = measured_traffic(spec.name, n)
+        if n in ("partial", "index_topk"):
+            kernels[n]["mfma_counters"] = mfma_counters(spec.name, n)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
@@ -465,12 +691,17 @@ def main():
                    "selection": "fused indexer + top-k" if path.fused_topk
                    else "score matrix + top-k",
                    "launch": "eager calls on one stream"},
-        "ms_per_step_without_markers": round(ms_plain, 4),
+        "timing": {"statistic": "median over the timed steps",
+                   "cache_flush": None if flush is None else "1 GiB read before each step, outside the events",
+                   "ms_min": round(min(step_ms), 4), "ms_mean": round(statistics.mean(step_ms), 4),
+                   "kernel_avg": "mean launch duration over the same steps"},
+        "ms_per_step_back_to_back": round(ms_plain, 4),
         "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
         "hbm": {"path_alg_bytes": int(path_bytes), "gbps": round(path_gbps, 1),
                 "frac": round(path_gbps / HBM_PEAK_GBPS, 4)},
         "kernels": kernels,
         "roofline": roof,
+        "measured_peaks": peaks,
     }
     if path.fused_topk:
         result["fused_select"] = {"fallback_tokens": fallback_tokens, "cap": path.cap,
@@ -485,11 +716,19 @@ def main():
         torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
+    cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl)
-    else:
-        result["cpu_baseline"] = None
+        cpu = cpu_baseline(wl)
+    result["cpu_baseline"] = cpu
+    if not args.no_extra and spec.name == "verify_fp8_64k":
+        pool.close()
+        del wl, path, pool, calls
+        torch.cuda.empty_cache()
+        print("[bench] prefill chunk", file=sys.stderr, flush=True)
+        result["prefill"] = bench_prefill(dsa, synth, dev, cus, flush, peaks)
+        print("[bench] shared-prefix tiles", file=sys.stderr, flush=True)
+        result["shared_prefix"] = bench_shared_prefix(dsa, synth, dev, cus, flush)
     print(json.dumps(result), flush=True)
 
 

@@ -69,3 +69,22 @@ def test_stats_summary_sums_the_fused_selection(tmp_path):
     assert "some_other_kernel" not in out
     assert float(got["partial"][2]) == 460.0
     assert float(got["index_topk"][2]) == (20000 + 9000 + 400000 + 35000 + 4000) / 1e3
+
+
+def test_mfma_summary_from_counters(tmp_path):
+    """MFMA use per launch from a counter CSV: counted FLOPs (512 per MOPS
+    unit) over the dispatch time, busy share of the 1024 SIMDs' cycles."""
+    csv = tmp_path / "c.csv"
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"
+    rows = [head]
+    name = '"void (anonymous namespace)::partial_ws_kernel<1, true>(x)"'
+    # 1e9 MOPS units over 400 us -> 512e9 / 4e-4 s = 1280 TFLOP/s; busy 2.5e8 of 1e6 x 1024 cycles
+    for c, v in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e9), ("SQ_VALU_MFMA_BUSY_CYCLES", 2.56e8),
+                 ("GRBM_GUI_ACTIVE", 8e6), ("MfmaUtil", 25.0)):
+        rows.append(f"7,{name},{c},{v},1000,401000")
+    csv.write_text("\n".join(rows) + "\n")
+    out = bench.summarize_mfma(str(csv), "w", ["cmd"])
+    k = out["kernels"]["partial"]
+    assert k["mfma_tflops_counted"] == 1280.0
+    assert k["busy_cycles_frac"] == 0.25
+    assert k["mfma_util"] == 0.25
