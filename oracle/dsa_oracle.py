@@ -43,6 +43,14 @@ silent (each is listed with its reason in the design notes of the repository):
     the even code, saturating at 448; the row's 28 pad bytes are zero.  The
     scale and x / scale are formed in fp32 (the precision in which the GPU
     decides the code); the rounding to E4M3FN is exact.
+  * Q8 prefill (LMSYS page, section 4 "Prefill dataflow optimization", and its
+    configuration table: FP8 query against the FP8 KV cache for prefill; the
+    query quantizer is not spelled out): one fp32 scale per query head over
+    its 576 elements, scale = amax / 448 (1 for an all-zero head) and
+    code = E4M3FN(q / scale) with the cache's rounding rule.  The score is the
+    product of the codes times both scales, i.e. the attention above with q
+    replaced by its dequantized value decode(code) * scale; the value sum is
+    unchanged.
 
 All floating point here is float64 (numpy).  Indexer scores are returned as
 float32 after an exact float64 computation (integer-valued inputs keep every
@@ -344,6 +352,38 @@ def quantize_fp8_row(x) -> tuple[np.ndarray, np.ndarray]:
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     y = (x32 / scale[:, None]).astype(np.float32)
     return e4m3fn_encode(y).reshape(D_QK), scale
+
+
+def quantize_q8(q) -> tuple[np.ndarray, np.ndarray]:
+    """Q8 query quantizer: q [..., 576] (any float input; the GPU path takes
+    bf16) -> (codes uint8 [..., 576], scales float32 [...]), one scale per
+    query head, formed like the cache's per-group scale: amax / 448 in fp32,
+    1 when the head is all zero, codes = E4M3FN(q / scale) with q / scale in
+    fp32."""
+    x32 = np.asarray(q, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[..., None]).astype(np.float32)
+    return e4m3fn_encode(y), scale
+
+
+def dequantize_q8(codes, scales) -> np.ndarray:
+    """decode(code) * scale in float64: the query the Q8 score multiplies
+    (the product of two codes times the two scales equals this value times
+    the dequantized cache element exactly)."""
+    return _E4M3[np.asarray(codes)] * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def token_path_q8(pool: PoolView, page_row, pos: int, idx, q_codes, q_scales,
+                  sm_scale: float, tile: int = 64):
+    """Q8 sparse attention of one query token over given index columns: the
+    attention of the dequantized FP8 query, one split.
+    Returns dict(o [64,512] f64, lse [64] f64)."""
+    o_p, lse_p = partial(dequantize_q8(q_codes, q_scales), np.asarray(idx), pos,
+                         lambda cols: pool.latent_rows(page_row, cols),
+                         sm_scale, tile, 1)
+    o, lse = combine(o_p, lse_p)
+    return dict(o=o, lse=lse)
 
 
 def append_rows(pool: PoolView, page_table: np.ndarray, req, pos, latent, keys=None):
