@@ -17,6 +17,9 @@
  *             weighted value sum; KV tile 32 or 128; index width not padded
  *             physically; splits add intermediate writes merged by Combine;
  *             dispatch from architecture, layout and query parallelism).
+ *   [LMSYS-4] same page, section 4 "Prefill dataflow optimization" and the
+ *             prefill configuration table (Q8 sparse attention: the DSA
+ *             prefill backend takes an FP8 query over the FP8 E4M3 KV cache).
  *   [VLLM]    "A million-token context on 16 H200s", Interpretation (MLA's
  *             latent KV row is shared by all 64 heads).
  *   [SGL]     SGLang cookbook "GLM-5.3-Flash", section 2 "Size both memory
@@ -286,6 +289,33 @@ dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_table, int32
                           int32_t num_tokens, const uint16_t* q, const int32_t* idx,
                           int32_t width, float sm_scale, int32_t kv_tile, uint16_t* out,
                           float* lse, void* stream);
+
+/* Q8 prefill [LMSYS-4 "Prefill dataflow optimization": the prefill attention
+ * takes an FP8 query against the FP8 KV cache; the query quantizer is not
+ * spelled out by the pages, the reading here: one fp32 scale per (token,
+ * head) over its 576 elements, scale = amax/448 (1 for an all-zero head),
+ * code = E4M3FN(q/scale) rounded to nearest, ties to even, saturating at 448,
+ * the same rounding as the cache rows].
+ *
+ * dsa_quantize_q8: q bf16 [num_tokens,64,576] (2-byte aligned) -> q_codes
+ * uint8 [num_tokens,64,576] and q_scales fp32 [num_tokens,64] (4-byte
+ * aligned).  Caller-owned device buffers; num_tokens = 0 launches nothing.
+ *
+ * dsa_sparse_mla_q8: the attention of dsa_sparse_mla (one split, final bf16
+ * output and natural-log lse, same index validity rules) with the score
+ *   z_j = sm_scale * q_scale[t,h] * sum_d code[t,h,d] * K(idx_j)[d]
+ * i.e. q replaced by its dequantized value decode(code) * q_scale; the value
+ * sum uses the dequantized latent as in dsa_sparse_mla.  FP8 pools only
+ * (a BF16 pool is DSA_ERR_INVALID_ARG).  Tiles of 32 rows; no kv_tile or
+ * split arguments.  q_codes 16-byte aligned; q_scales, idx, out, lse 4-byte.
+ * Errors as dsa_sparse_mla. */
+dsa_status dsa_quantize_q8(const uint16_t* q, int32_t num_tokens, uint8_t* q_codes,
+                           float* q_scales, void* stream);
+dsa_status dsa_sparse_mla_q8(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                             const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
+                             int32_t num_tokens, const uint8_t* q_codes, const float* q_scales,
+                             const int32_t* idx, int32_t width, float sm_scale, uint16_t* out,
+                             float* lse, void* stream);
 
 /* Combine [LMSYS-3]: per token and head,
  *   lse = ln sum_s exp(lse_part_s),  out = sum_s exp(lse_part_s - lse) * o_part_s

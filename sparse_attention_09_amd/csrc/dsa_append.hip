@@ -27,27 +27,6 @@ constexpr int kGroups = DSA_D_QK / 64;         // 9
 constexpr int kFp8Stride = 640;
 constexpr int kBf16Stride = 2 * DSA_D_QK;
 
-// Nearest E4M3FN code of a finite fp32 value (ties to even, |y| saturated at
-// 448, sign from y).
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // below 2^-6 the grid is the subnormals, step 2^-9: a*512 is exact and
-    // rint rounds half to even (8 is the smallest normal, code 0x08)
-    code = uint32_t(__builtin_rintf(a * 512.f));
-  } else {
-    const uint32_t bits = __float_as_uint(a);
-    const uint32_t e = (bits >> 23) - 127u + 7u;   // biased E4M3 exponent, 1..15
-    const uint32_t m = bits & 0x7FFFFFu;
-    const uint32_t m3 = m >> 20, rem = m & 0xFFFFFu;
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
-    code = min((e << 3) + m3 + up, 0x7Eu);       // a mantissa carry moves up the exponent
-  }
-  return sign | code;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -81,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
       scale[g] = amax > 0.f ? amax / 448.f : 1.f;
     }
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) row[64 * g + lane] = uint8_t(e4m3_encode(v[g] / scale[g]));
+    for (int g = 0; g < kGroups; ++g) row[64 * g + lane] = uint8_t(dsa::e4m3_encode(v[g] / scale[g]));
     // scales at byte 576 (lanes 0..8), zero padding up to byte 640 (lanes 9..15)
     float sv = 0.f;
 #pragma unroll
@@ -99,7 +78,49 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   }
 }
 
+// Q8 query quantizer [LMSYS page, section 4 "Prefill dataflow optimization":
+// the prefill attention takes an FP8 query against the FP8 cache; the
+// quantizer is not spelled out].  One fp32 scale per (token, head) over its
+// 576 elements, scale = amax / 448 (1 for an all-zero head), codes by the
+// cache's rule.  One wave per (token, head), lane l holding elements 64g + l,
+// so the amax is one wave reduction and each group's codes one 64-byte store.
+__global__ __launch_bounds__(kThreads) void quantize_q8_kernel(const uint16_t* __restrict__ q,
+                                                              int64_t rows,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (i >= rows) return;
+  const uint16_t* x = q + i * DSA_D_QK;
+  float v[kGroups];
+  float amax = 0.f;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    v[g] = dsa::bf16_bits_to_f32(x[64 * g + lane]);
+    amax = fmaxf(amax, fabsf(v[g]));
+  }
+  amax = wave_max(amax);
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  uint8_t* row = codes + i * DSA_D_QK;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) row[64 * g + lane] = uint8_t(dsa::e4m3_encode(v[g] / scale));
+  if (lane == 0) scales[i] = scale;
+}
+
 }  // namespace
+
+extern "C" dsa_status dsa_quantize_q8(const uint16_t* q, int32_t num_tokens, uint8_t* q_codes,
+                                      float* q_scales, void* stream) {
+  const dsa_status s = dsa::check_quantize_q8(q, num_tokens, q_codes, q_scales);
+  if (s != DSA_OK || num_tokens == 0) return s == DSA_OK ? dsa::ok() : s;
+  const int64_t rows = int64_t(num_tokens) * DSA_HEADS;
+  hipLaunchKernelGGL(quantize_q8_kernel, dim3(unsigned((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(kThreads), 0, static_cast<hipStream_t>(stream), q, rows, q_codes, q_scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string("dsa_quantize_q8: launch failed: ") + hipGetErrorString(e));
+  return dsa::ok();
+}
 
 extern "C" dsa_status dsa_kv_append(const dsa_pool* pool, const int32_t* page_table,
                                     int32_t pt_stride, int32_t num_reqs, const int32_t* req,

@@ -54,6 +54,28 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t codes, float out[4]) {
   out[3] = hi[1];
 }
 
+// Nearest E4M3FN code of a finite fp32 value (ties to even, |y| saturated at
+// 448, sign from y), with integer operations on the fp32 bits: exact and
+// independent of any hardware conversion mode.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below 2^-6 the grid is the subnormals, step 2^-9: a*512 is exact and
+    // rint rounds half to even (8 is the smallest normal, code 0x08)
+    code = uint32_t(__builtin_rintf(a * 512.f));
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t e = (bits >> 23) - 127u + 7u;   // biased E4M3 exponent, 1..15
+    const uint32_t m = bits & 0x7FFFFFu;
+    const uint32_t m3 = m >> 20, rem = m & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
+    code = min((e << 3) + m3 + up, 0x7Eu);       // a mantissa carry moves up the exponent
+  }
+  return sign | code;
+}
+
 // Max / sum over lanes i, i^16, i^32, i^48 (the four 16-lane rows of a
 // wave), every lane receiving the result: v_permlane32_swap then
 // v_permlane16_swap each pair a lane with its partner in one VALU op (no LDS

@@ -104,6 +104,13 @@ dsa_status check_partial(const char* who, const dsa_pool* pool, const int32_t* p
                          const int32_t* idx, int32_t width, float sm_scale, int32_t kv_tile,
                          int32_t num_splits, bool final_form, const void* out_a,
                          const void* out_b);
+dsa_status check_quantize_q8(const uint16_t* q, int32_t num_tokens, const uint8_t* q_codes,
+                             const float* q_scales);
+dsa_status check_sparse_mla_q8(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                               const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
+                               int32_t num_tokens, const uint8_t* q_codes, const float* q_scales,
+                               const int32_t* idx, int32_t width, float sm_scale,
+                               const uint16_t* out, const float* lse);
 dsa_status check_combine(const char* who, const float* o_part, const float* lse_part,
                          int32_t num_tokens, int32_t parts, const uint16_t* out, const float* lse);
 dsa_status check_dcp_merge(int32_t num_shards, int32_t num_tokens, int32_t k,

@@ -87,6 +87,8 @@ struct PartialArgs {
   int num_reqs;
   const int32_t* tok_pos;
   const uint16_t* q;
+  const uint8_t* q8;     // Q8 path: E4M3 query codes [T,64,576]
+  const float* q8_scale; // and one scale per (token, head)
   const int32_t* idx;
   int width;
   float scale_log2;      // sm_scale * log2(e)
@@ -121,6 +123,15 @@ __device__ __forceinline__ void put_lse(const PartialArgs& a, int64_t ts, int he
 // wave instruction read whole 128-byte lines of one or two rows.
 template <int KV, int NR, int NT>
 struct Stage;
+
+// 4 E4M3 codes times their group scale -> 4 bf16 (two dwords): exact decode,
+// one fp32 product, round to nearest even.
+__device__ __forceinline__ u32x2 dq4_bf16(uint32_t codes, float scale) {
+  float f[4];
+  dsa::fp8x4_to_f32(codes, f);
+  return u32x2{dsa::pack_bf16x2(f[0] * scale, f[1] * scale),
+               dsa::pack_bf16x2(f[2] * scale, f[3] * scale)};
+}
 
 // FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.  Latent chunk
 // q (16 codes) is row q/32, columns 16(q%32)..+16, with the scale of group
@@ -183,13 +194,7 @@ struct Stage<DSA_KV_FP8_E4M3_S64, NR, NT> {
     }
   }
 
-  // 4 codes -> 4 bf16 (two dwords)
-  __device__ __forceinline__ static u32x2 dq4(uint32_t codes, float scale) {
-    float f[4];
-    dsa::fp8x4_to_f32(codes, f);
-    return u32x2{dsa::pack_bf16x2(f[0] * scale, f[1] * scale),
-                 dsa::pack_bf16x2(f[2] * scale, f[3] * scale)};
-  }
+  __device__ __forceinline__ static u32x2 dq4(uint32_t codes, float scale) { return dq4_bf16(codes, scale); }
 
   // 16 codes -> 16 bf16 = logical chunks `chunk` (even) and `chunk`+1 of
   // row r (physically k_phys(chunk) and k_phys(chunk) ^ 1)
@@ -299,15 +304,16 @@ struct Stage<DSA_KV_BF16, NR, NT> {
 };
 
 // Physical rows (page*64 + slot, or -1 when masked) of index columns
-// [cc, cc + kRowChunk) of token t, written to rows[]; with a bias array, also
+// [cc, cc + N) of token t, written to rows[]; with a bias array, also
 // 0 for a valid row and -inf for a masked one.  *last (reset to -1 by the
 // caller) receives the largest chunk-relative column with a valid row.
-// nthreads must divide kRowChunk.
+// nthreads must divide N (the column count, kRowChunk by default).
+template <int N = kRowChunk>
 __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int req, int pos, int cc,
                                              int cend, int32_t* rows, int tid, int nthreads,
                                              int* last, float* bias = nullptr) {
   const int lane = tid & 63;
-  for (int i = tid; i < kRowChunk; i += nthreads) {
+  for (int i = tid; i < N; i += nthreads) {
     const int col = cc + i;
     int phys = -1;
     if (col < cend) {
@@ -1075,6 +1081,379 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Q8 prefill ["Accelerating GLM-5.3-Flash on H200", section 4 "Prefill
+// dataflow optimization": the prefill attention multiplies an FP8 query with
+// the FP8 cache].  S = K Q^T runs on gfx950's 32x32x64 f8f6f4 MFMA, the FP8
+// form with twice the bf16 rate.  Its 64-deep contraction is exactly one
+// scale group of a cache row, so the product of group g's codes lands in a
+// fresh accumulator and is added into the score times that row's fp32 group
+// scale (exact up to fp32 rounding: no rescaling of codes); the query's one
+// scale per head multiplies the finished score.  The value product stays on
+// bf16 with V dequantized once per tile, as in the bf16 path.
+//
+// One workgroup per token, 8 waves (wave w runs on SIMD w % 4), tiles of 32
+// rows:
+//   * score waves 0, 1: heads 32w..+32 against the tile's 32 rows; lane l holds
+//     head 32w + l%32 and rows 8q + 4(l/32) + j (q, j < 4), the query codes of
+//     its head stay in registers; online softmax with the running reference
+//     max of the bf16 kernels;
+//   * value waves: O for all 64 heads on a slice of the output columns.  Waves
+//     2, 3, 6, 7 (SIMDs 2 and 3, which hold no score wave) take 96 columns each
+//     and gather and dequantize the tile's latent codes; waves 4 and 5 (beside
+//     the score waves) take 64 columns and the rope codes, so each SIMD gets a
+//     similar share of matrix and vector work.
+// Per tile the raw codes go to a ring of two buffers (score waves read tile j
+// while tile j+1 is written) with their scales beside them, the dequantized
+// latent to a ring of three (value waves read tile j-1) and P to a ring of
+// two; one barrier per tile.
+constexpr int kTileQ8 = 32;
+constexpr int kRowChunkQ8 = 1024;              // index columns resolved at once (LDS budget)
+constexpr int kK8Stride = DSA_D_QK + 16;       // bytes per raw-code row: 37 16-byte chunks
+constexpr int kVStrideQ8 = DSA_D_LATENT + 16;  // bf16 per V row: 1056 bytes = 33 x 32
+constexpr int kQ8Groups = DSA_D_QK / 64;       // 9 scale groups = 9 MFMA k-steps
+constexpr int kQ8Depth = 3;                    // tiles gathered ahead into registers
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Raw-code tile: logical 16-byte chunk x of row r at physical chunk
+// x ^ bit4(r).  A score lane (row m = l%32, half h = l/32) reads logical
+// chunks 4g + h and 4g + 2 + h of group g; a 32-lane pass of a 16-byte read
+// (lanes 0..15 with 48..63, then 16..47) meets rows m and m + 16 of opposite
+// halves, which the flip puts in the same physical chunk, and with the odd
+// stride the 32 rows fall on 32 distinct bank slots.  Staging writes (8 lanes
+// on 8 consecutive chunks of a row) are conflict-free as well.
+// V tile: logical bf16 chunk x (8 values) of row r at k_phys(x), rows 33
+// 32-byte units apart (odd), which keeps the transpose reads and the staging
+// writes conflict-free, as in the bf16 K tile.
+struct SmemQ8 {
+  uint8_t k8[2][kTileQ8 * kK8Stride];          // raw E4M3 codes
+  float sc[2][kQ8Groups][kTileQ8];             // their group scales, group-major
+  uint16_t v[3][kTileQ8 * kVStrideQ8];         // dequantized latent (V), bf16
+  uint16_t p[2][DSA_HEADS * kPStrideWS];       // P in the PV operand's row order
+  float alpha[2][DSA_HEADS];
+  int32_t rows[kRowChunkQ8];
+  float bias[kRowChunkQ8];
+  float fin_l[DSA_HEADS];
+  int last;
+};
+static_assert(sizeof(SmemQ8) <= 160 * 1024, "Q8 tiles exceed the LDS");
+
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b) {
+  const f32x16 zero = {};
+  // E4M3 operands (format 0), block scales 2^0 (E8M0 127)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Max / sum of lanes l and l ^ 32, every lane receiving the result: after
+// v_permlane32_swap one result holds lane l % 32's value and the other lane
+// l % 32 + 32's, in every lane.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Latent gather of the four wide value waves (256 threads, index sid): chunk
+// q = sid + 256i (i < 4) is row q / 32, codes 16(q % 32)..+16, group (q % 32) / 4.
+// Invalid rows load row 0 and store zero codes and scales.
+struct Q8Latent {
+  u32x4 code[4];
+  float scale[4];
+  uint32_t ok;
+  __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int sid) {
+    ok = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = sid + 256 * i;
+      const int phys = rows[q >> 5];
+      ok |= uint32_t(phys >= 0) << i;
+      const uint8_t* row = latent + int64_t(max(phys, 0)) * 640;
+      code[i] = *reinterpret_cast<const u32x4*>(row + 16 * (q & 31));
+      scale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* k8, float* sc, uint16_t* v, int sid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = sid + 256 * i, r = q >> 5, c = q & 31;
+      const bool okb = (ok >> i) & 1u;
+      const u32x4 cd = okb ? code[i] : u32x4{0, 0, 0, 0};
+      const float s = okb ? scale[i] : 0.f;
+      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) = cd;
+      // bf16 chunks 2c, 2c + 1 at k_phys(2c), k_phys(2c) ^ 1
+      uint16_t* vr = v + r * kVStrideQ8 + 8 * k_phys(2 * c);
+      const u32x2 a0 = dq4_bf16(cd[0], s), a1 = dq4_bf16(cd[1], s);
+      *reinterpret_cast<u32x4*>(vr) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      const u32x2 b0 = dq4_bf16(cd[2], s), b1 = dq4_bf16(cd[3], s);
+      *reinterpret_cast<u32x4*>(v + r * kVStrideQ8 + 8 * (k_phys(2 * c) ^ 1)) =
+          u32x4{b0[0], b0[1], b1[0], b1[1]};
+      if ((c & 3) == 0) sc[(c >> 2) * kTileQ8 + r] = s;
+    }
+  }
+};
+
+// Rope gather of the two narrow value waves (128 threads): chunk q = sid is
+// row q / 4, rope codes 16(q % 4)..+16; the q % 4 == 0 thread also writes the
+// rope group's scale.
+struct Q8Rope {
+  u32x4 code;
+  float scale;
+  bool ok;
+  __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int sid) {
+    const int phys = rows[sid >> 2];
+    ok = phys >= 0;
+    const uint8_t* row = latent + int64_t(max(phys, 0)) * 640;
+    code = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (sid & 3));
+    scale = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+  }
+  __device__ __forceinline__ void store(uint8_t* k8, float* sc, uint16_t*, int sid) const {
+    const int r = sid >> 2, c = DSA_D_LATENT / 16 + (sid & 3);
+    *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) =
+        ok ? code : u32x4{0, 0, 0, 0};
+    if ((sid & 3) == 0) sc[8 * kTileQ8 + r] = ok ? scale : 0.f;
+  }
+};
+
+// Score waves stage nothing.
+struct Q8NoStage {
+  __device__ __forceinline__ void load(const uint8_t*, const int32_t*, int) {}
+  __device__ __forceinline__ void store(uint8_t*, float*, uint16_t*, int) const {}
+};
+
+// The tile loop shared by all roles (identical barriers): per chunk of
+// kRowChunkQ8 index columns the rows are resolved, tiles 0..kQ8Depth-1
+// gathered and tile 0 stored; iteration j (in whole groups of three, so the
+// gathers form one straight-line stream) calls work(j, ntile, P), stores tile
+// j + 1 (codes and scales into buffer (j + 1) % 2, V into (j + 1) % 3),
+// gathers tile j + 1 + kQ8Depth and waits at the barrier.  Past the last tile
+// the row indices are clamped and the stores refill buffers nobody reads.
+template <class Stager, class Work>
+__device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, int t, int req,
+                                            int pos, int tid, int sid, Work&& work) {
+  constexpr int kD = kQ8Depth;
+  Stager st[kD];
+  for (int cc = 0; cc < a.width; cc += kRowChunkQ8) {
+    const int cend = min(a.width, cc + kRowChunkQ8);
+    __syncthreads();
+    if (tid == 0) sm.last = -1;
+    __syncthreads();
+    resolve_rows<kRowChunkQ8>(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
+    __syncthreads();
+    const int ntile = (sm.last + kTileQ8) / kTileQ8;
+    if (ntile == 0) continue;
+    auto tile_rows = [&](int i) { return sm.rows + min(i, ntile - 1) * kTileQ8; };
+    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), sid); });
+    st[0].store(sm.k8[0], &sm.sc[0][0][0], sm.v[0], sid);
+    st[0].load(a.latent, tile_rows(kD), sid);
+    __syncthreads();
+    for (int j0 = 0; j0 <= ntile; j0 += 3) {
+      dsa::static_for<3>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        const int j = j0 + p;
+        constexpr int si = (p + 1) % kD;
+        work(j, ntile, P);
+        const int kn = (j + 1) & 1;
+        st[si].store(sm.k8[kn], &sm.sc[kn][0][0], sm.v[(p + 1) % 3], sid);
+        st[si].load(a.latent, tile_rows(j + 1 + kD), sid);
+        __syncthreads();
+      });
+    }
+  }
+}
+
+// Value role: O for all 64 heads on columns d0..d0 + 16NB (PV of tile j - 1 in
+// iteration j, as in the bf16 warp-specialized kernel).
+template <int NB, class Stager>
+__device__ __forceinline__ void q8_value(const PartialArgs& a, SmemQ8& sm, int t, int req, int pos,
+                                         int tid, int sid, int d0) {
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  f32x4 o[4][NB];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transpose read of rows 4g + c/4 (+16), columns d0 + 16nb + 4(c%4): logical
+  // chunk x = d0/8 + 2nb + (c%4)/2, physical k_phys(x) (bit 3 of the even
+  // chunk, the same for the wave, picks the lane base)
+  const int vrow = (4 * g + (c >> 2)) * kVStrideQ8 + d0 + 4 * (c & 1);
+  const int vlane0 = vrow + 8 * ((c & 3) >> 1);
+  const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
+  const int xb = d0 >> 3;
+  q8_pipeline<Stager>(a, sm, t, req, pos, tid, sid, [&](int j, int ntile, auto P) {
+    constexpr int p = decltype(P)::value;
+    if (j >= 1 && j <= ntile) {
+      const int jp = j - 1;
+      f32x4 al[4];
+      bool rescale = false;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        al[hb] = *reinterpret_cast<const f32x4*>(sm.alpha[jp & 1] + 16 * hb + 4 * g);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[hb][jj] != 1.f;
+      }
+      if (__any(rescale)) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[hb][jj];
+      }
+      const uint16_t* pb = sm.p[jp & 1];
+      u32x4 pa[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        pa[hb] = *reinterpret_cast<const u32x4*>(pb + (16 * hb + c) * kPStrideWS + 8 * (g ^ p_swz(c)));
+      const uint16_t* vt = sm.v[(p + 2) % 3];
+      auto vread = [&](int nb) {
+        const int x = xb + 2 * nb;
+        const uint16_t* vp = vt + ((x >> 3) & 1 ? vlane1 : vlane0) + 16 * nb;
+        const u32x2 lo2 = lds_read_tr16(vp);
+        const u32x2 hi2 = lds_read_tr16(vp + 16 * kVStrideQ8);
+        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      };
+      u32x4 vb = vread(0);
+      dsa::static_for<NB>([&](auto NBI) {
+        constexpr int nb = decltype(NBI)::value;
+        u32x4 vn;
+        if constexpr (nb + 1 < NB) vn = vread(nb + 1);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hb][nb] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[hb]), dsa::as_bf16x8(vb), o[hb][nb]);
+        if constexpr (nb + 1 < NB) vb = vn;
+      });
+    }
+  });
+  __syncthreads();   // the score waves have written each head's sum
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int hh = 16 * hb + 4 * g + jj;
+      const float l = sm.fin_l[hh];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) put_out<true>(a, t, hh, d0 + 16 * nb + c, o[hb][nb][jj] * inv);
+    }
+}
+
+__global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(16))) SmemQ8 sm;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int req = request_of(a, t);
+  const int pos = a.tok_pos[t];
+
+  if (wave < 2) {
+    // ---- score wave: heads 32w + n; MFMA A = code rows (row m = lane % 32),
+    // B = query codes (head n = lane % 32), both halves h = lane / 32 holding
+    // logical chunks 4g + h and 4g + 2 + h of group g
+    const int n = lane & 31, h = lane >> 5;
+    const int head = 32 * wave + n;
+    i32x8 qf[kQ8Groups];
+    {
+      const uint8_t* qs = a.q8 + (int64_t(t) * DSA_HEADS + head) * DSA_D_QK + 16 * h;
+#pragma unroll
+      for (int g = 0; g < kQ8Groups; ++g)
+        qf[g] = cat8(*reinterpret_cast<const u32x4*>(qs + 64 * g),
+                     *reinterpret_cast<const u32x4*>(qs + 64 * g + 32));
+    }
+    const float cq = a.q8_scale[int64_t(t) * DSA_HEADS + head] * a.scale_log2;
+    const int ka = n * kK8Stride + 16 * (h ^ ((n >> 4) & 1));
+    const int sw = p_swz(head & 15);
+    float m_run = kNegInf, l_run = 0.f;
+    q8_pipeline<Q8NoStage>(a, sm, t, req, pos, tid, 0, [&](int j, int ntile, auto) {
+      if (j < ntile) {
+        const uint8_t* k8 = sm.k8[j & 1];
+        const float* sc = &sm.sc[j & 1][0][0];
+        auto aread = [&](int g) {
+          return cat8(*reinterpret_cast<const u32x4*>(k8 + ka + 64 * g),
+                      *reinterpret_cast<const u32x4*>(k8 + ka + 64 * g + 32));
+        };
+        // acc[4q + jj] = score of row 8q + 4h + jj: sum over groups of the
+        // group's code product times the row's group scale
+        f32x16 acc, tmp[2];
+        auto promote = [&](int g, const f32x16& pg) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 s = *reinterpret_cast<const f32x4*>(sc + g * kTileQ8 + 8 * q + 4 * h);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              acc[4 * q + jj] = g == 0 ? pg[4 * q + jj] * s[jj] : fmaf(pg[4 * q + jj], s[jj], acc[4 * q + jj]);
+          }
+        };
+        i32x8 af[2];
+        af[0] = aread(0);
+        dsa::static_for<kQ8Groups>([&](auto G) {
+          constexpr int g = decltype(G)::value;
+          if constexpr (g + 1 < kQ8Groups) af[(g + 1) & 1] = aread(g + 1);
+          tmp[g & 1] = mfma32x32x64_fp8(af[g & 1], qf[g]);
+          if constexpr (g >= 1) promote(g - 1, tmp[(g - 1) & 1]);
+        });
+        promote(kQ8Groups - 1, tmp[(kQ8Groups - 1) & 1]);
+        // log2-domain scores (-inf on masked rows) and the tile max of the head
+        float z[16];
+        float tmax = kNegInf;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(sm.bias + j * kTileQ8 + 8 * q + 4 * h);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            z[4 * q + jj] = fmaf(acc[4 * q + jj], cq, b[jj]);
+            tmax = fmaxf(tmax, z[4 * q + jj]);
+          }
+        }
+        tmax = halves_max(tmax);
+        float alpha = 1.f;
+        if (tmax > m_run + kRescaleThreshold) {
+          if (m_run != kNegInf) alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+          l_run *= alpha;
+          m_run = tmax;
+        }
+        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(z[r] + neg_m);
+          l_run += pr[r];
+        }
+        // PV operand position 8g' + 4e + jj holds row 16e + 4g' + jj: rows of
+        // q = 0 and 2 fill chunk h of the head's P row, q = 1 and 3 chunk 2 + h
+        uint16_t* prow = sm.p[j & 1] + head * kPStrideWS;
+        *reinterpret_cast<u32x4*>(prow + 8 * (h ^ sw)) =
+            u32x4{dsa::pack_bf16x2(pr[0], pr[1]), dsa::pack_bf16x2(pr[2], pr[3]),
+                  dsa::pack_bf16x2(pr[8], pr[9]), dsa::pack_bf16x2(pr[10], pr[11])};
+        *reinterpret_cast<u32x4*>(prow + 8 * ((2 + h) ^ sw)) =
+            u32x4{dsa::pack_bf16x2(pr[4], pr[5]), dsa::pack_bf16x2(pr[6], pr[7]),
+                  dsa::pack_bf16x2(pr[12], pr[13]), dsa::pack_bf16x2(pr[14], pr[15])};
+        if (h == 0) sm.alpha[j & 1][head] = alpha;
+      }
+    });
+    const float l = halves_sum(l_run);
+    if (h == 0) {
+      sm.fin_l[head] = l;
+      put_lse<true>(a, t, head, l > 0.f ? (m_run + log2f(l)) * kLn2 : kNegInf);
+    }
+    __syncthreads();
+  } else if (wave == 4 || wave == 5) {
+    q8_value<4, Q8Rope>(a, sm, t, req, pos, tid, tid - 256, 192 + 64 * (wave - 4));
+  } else {
+    const int hw = wave < 4 ? wave - 2 : wave - 4;   // waves 2, 3, 6, 7 -> 0..3
+    const int d0 = hw < 2 ? 96 * hw : 320 + 96 * (hw - 2);
+    q8_value<6, Q8Latent>(a, sm, t, req, pos, tid, 64 * hw + lane, d0);
+  }
+}
+
 template <int KV, int TILE, bool kFinal>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
   if constexpr (TILE == kTile4)
@@ -1180,6 +1559,8 @@ static dsa_status run_partial(const char* who, const dsa_pool* pool, const int32
   a.num_reqs = num_reqs;
   a.tok_pos = tok_pos;
   a.q = q;
+  a.q8 = nullptr;
+  a.q8_scale = nullptr;
   a.idx = idx;
   a.width = width;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
@@ -1235,6 +1616,49 @@ extern "C" dsa_status dsa_sparse_mla(const dsa_pool* pool, const int32_t* page_t
   return run_partial("dsa_sparse_mla", pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
                      num_tokens, q, idx, width, sm_scale, kv_tile, 1, nullptr, nullptr, out, lse,
                      stream);
+}
+
+extern "C" dsa_status dsa_sparse_mla_q8(const dsa_pool* pool, const int32_t* page_table,
+                                        int32_t pt_stride, const int32_t* q_offsets,
+                                        int32_t num_reqs, const int32_t* tok_pos,
+                                        int32_t num_tokens, const uint8_t* q_codes,
+                                        const float* q_scales, const int32_t* idx, int32_t width,
+                                        float sm_scale, uint16_t* out, float* lse, void* stream) {
+  const char* who = "dsa_sparse_mla_q8";
+  dsa_status s = dsa::check_sparse_mla_q8(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos,
+                                          num_tokens, q_codes, q_scales, idx, width, sm_scale, out,
+                                          lse);
+  if (s != DSA_OK) return s;
+  if (num_tokens == 0) return dsa::ok();
+  s = dsa::deep_check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos, num_tokens,
+                            who, stream);
+  if (s != DSA_OK) return s;
+  PartialArgs a;
+  a.latent = reinterpret_cast<const uint8_t*>(pool->base + pool->layout.latent_plane_offset);
+  a.num_pages = pool->num_pages;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.q_offsets = q_offsets;
+  a.num_reqs = num_reqs;
+  a.tok_pos = tok_pos;
+  a.q = nullptr;
+  a.q8 = q_codes;
+  a.q8_scale = q_scales;
+  a.idx = idx;
+  a.width = width;
+  a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  a.cols_per_split = width;
+  a.splits = 1;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  a.out = out;
+  a.lse_out = lse;
+  hipLaunchKernelGGL(partial_q8_kernel, dim3(unsigned(num_tokens)), dim3(kThreadsV2), 0,
+                     static_cast<hipStream_t>(stream), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dsa::fail(DSA_ERR_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(e));
+  return dsa::ok();
 }
 
 static dsa_status run_combine(const char* who, const float* o_part, const float* lse_part,

@@ -215,6 +215,43 @@ dsa_status check_partial(const char* who, const dsa_pool* pool, const int32_t* p
   return DSA_OK;
 }
 
+dsa_status check_quantize_q8(const uint16_t* q, int32_t num_tokens, const uint8_t* q_codes,
+                             const float* q_scales) {
+  const char* who = "dsa_quantize_q8";
+  if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, S(who) + ": num_tokens < 0");
+  if (num_tokens == 0) return DSA_OK;
+  if (!q || !q_codes || !q_scales)
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": q, q_codes and q_scales must be non-null");
+  if (!aligned(q, 2) || !aligned(q_scales, 4))
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": q must be 2-byte and q_scales 4-byte aligned");
+  if ((int64_t(num_tokens) * DSA_HEADS + 3) / 4 > 0x7fffffff)
+    return fail(DSA_ERR_UNSUPPORTED, S(who) + ": too many tokens for one launch");
+  return DSA_OK;
+}
+
+dsa_status check_sparse_mla_q8(const dsa_pool* pool, const int32_t* page_table, int32_t pt_stride,
+                               const int32_t* q_offsets, int32_t num_reqs, const int32_t* tok_pos,
+                               int32_t num_tokens, const uint8_t* q_codes, const float* q_scales,
+                               const int32_t* idx, int32_t width, float sm_scale,
+                               const uint16_t* out, const float* lse) {
+  const char* who = "dsa_sparse_mla_q8";
+  dsa_status s = check_batch(pool, page_table, pt_stride, q_offsets, num_reqs, tok_pos, num_tokens, who);
+  if (s != DSA_OK) return s;
+  if (pool->kv_dtype != DSA_KV_FP8_E4M3_S64)
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": the Q8 path reads an FP8 pool");
+  if (width < 1) return fail(DSA_ERR_INVALID_ARG, S(who) + ": width must be >= 1");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": sm_scale must be finite and > 0");
+  if (num_tokens == 0) return DSA_OK;
+  if (!q_codes || !q_scales || !idx || !out || !lse)
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": q_codes, q_scales, idx, out and lse must be non-null");
+  if (!aligned(q_codes, 16) || !aligned(q_scales, 4) || !aligned(idx, 4) || !aligned(out, 4) ||
+      !aligned(lse, 4))
+    return fail(DSA_ERR_INVALID_ARG, S(who) + ": q_codes must be 16-byte aligned; q_scales, idx, "
+                                              "out and lse 4-byte");
+  return DSA_OK;
+}
+
 dsa_status check_combine(const char* who, const float* o_part, const float* lse_part,
                          int32_t num_tokens, int32_t parts, const uint16_t* out, const float* lse) {
   if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, S(who) + ": num_tokens < 0");

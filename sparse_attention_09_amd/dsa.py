@@ -40,7 +40,7 @@ EXPORTS = [
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
     "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
     "dsa_index_topk_workspace_bytes", "dsa_index_topk", "dsa_dcp_merge", "dsa_combine_shards",
-    "dsa_topk_noalloc",
+    "dsa_topk_noalloc", "dsa_quantize_q8", "dsa_sparse_mla_q8",
 ]
 
 
@@ -106,6 +106,9 @@ def lib() -> ctypes.CDLL:
                                              i32, vp, vp, vp]),
             "dsa_sparse_mla": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, f32, i32, vp, vp,
                                      vp]),
+            "dsa_quantize_q8": (i32, [vp, i32, vp, vp, vp]),
+            "dsa_sparse_mla_q8": (i32, [vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, f32, vp,
+                                        vp, vp]),
             "dsa_combine": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "dsa_kv_append": (i32, [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]),
             "dsa_index_topk_workspace_bytes": (sz, [i32, i32, i32]),
@@ -365,6 +368,48 @@ def sparse_mla(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_scale: flo
                                 _ptr(q_offsets), B, _ptr(tok_pos), T, _ptr(q), _ptr(idx),
                                 idx.shape[-1], float(sm_scale), kv_tile, _ptr(out), _ptr(lse),
                                 _stream(dev)))
+    return out, lse
+
+
+def quantize_q8(q: torch.Tensor, codes=None, scales=None):
+    """Q8 query: E4M3 codes [T, 64, 576] (uint8) and one fp32 scale per
+    (token, head) [T, 64] from the bf16 query."""
+    dev = q.device
+    T = q.shape[0]
+    _need(q, "q", torch.bfloat16, dev, (T, HEADS, D_QK))
+    if codes is None:
+        codes = torch.empty((T, HEADS, D_QK), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    _need(codes, "codes", torch.uint8, dev, (T, HEADS, D_QK))
+    _need(scales, "scales", torch.float32, dev, (T, HEADS))
+    _check(lib().dsa_quantize_q8(_ptr(q), T, _ptr(codes), _ptr(scales), _stream(dev)))
+    return codes, scales
+
+
+def sparse_mla_q8(pool: Pool, page_table, q_offsets, tok_pos, q_codes, q_scales, idx,
+                  sm_scale: float, out=None, lse=None):
+    """Q8 sparse MLA (FP8 query codes x FP8 cache rows), one split, straight to
+    the bf16 output and lse."""
+    dev = pool.device
+    T = tok_pos.numel()
+    B = q_offsets.numel() - 1
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(tok_pos, "tok_pos", torch.int32, dev)
+    _need(q_codes, "q_codes", torch.uint8, dev, (T, HEADS, D_QK))
+    _need(q_scales, "q_scales", torch.float32, dev, (T, HEADS))
+    _need(idx, "idx", torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, HEADS, D_LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (T, HEADS, D_LATENT))
+    _need(lse, "lse", torch.float32, dev, (T, HEADS))
+    _check(lib().dsa_sparse_mla_q8(pool.handle, _ptr(page_table), page_table.shape[-1],
+                                   _ptr(q_offsets), B, _ptr(tok_pos), T, _ptr(q_codes),
+                                   _ptr(q_scales), _ptr(idx), idx.shape[-1], float(sm_scale),
+                                   _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 
 
