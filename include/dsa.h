@@ -89,6 +89,10 @@ enum {
   DSA_KV_BF16 = 0,         /* 576 bf16 per row */
   DSA_KV_FP8_E4M3_S64 = 1  /* 576 OCP E4M3FN codes + 9 fp32 scales (one per 64) */
 };
+/* FP8 rows: element d = decode(code[d]) * scale[d/64].  The scales are
+ * powers of two (what dsa_kv_append writes): the attention kernels apply them
+ * as block scales, i.e. only their exponent, so a row written with any other
+ * fp32 scale is read with that scale rounded down to a power of two. */
 
 int32_t dsa_abi_version(void);
 /* Message of the last non-OK status on this thread ("" if none). */
@@ -358,9 +362,10 @@ dsa_status dsa_combine_shards(const float* o_part, const float* lse_part, int32_
  *   keys:   bf16 [n,128] indexer keys, 16-byte aligned, or NULL to leave the
  *           indexer plane untouched.
  * FP8 pools (reading of the quantizer, not spelled out by the pages): per 64
- * consecutive elements scale = amax/448 in fp32 (1 for an all-zero group),
- * code = E4M3FN(x/scale) rounded to the nearest finite value, ties to the
- * even code, saturated at 448 (x/scale formed in fp32); the nine scales
+ * consecutive elements the scale is the smallest power of two 2^k
+ * (k >= -126) with amax <= 448 * 2^k (1 for an all-zero group), stored as
+ * fp32, and code = E4M3FN(x/scale) rounded to the nearest finite value, ties
+ * to the even code (x/scale is exact and within +-448); the nine scales
  * follow the codes and the 28 pad bytes are written as 0.  BF16 pools: the
  * 576 values are copied.  Rows whose request (outside [0,num_reqs)),
  * position (negative or past the page table) or page id (outside the pool)

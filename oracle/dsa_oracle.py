@@ -37,12 +37,13 @@ silent (each is listed with its reason in the design notes of the repository):
   * FP8 rows: 576 OCP E4M3FN codes followed by nine little-endian fp32 scales,
     one per 64 consecutive elements; value = decode(code) * scale;
   * writing a new token into the cache (SGLang cookbook: FP8 KV cache by
-    default; the quantizer itself is not spelled out): per group of 64,
-    scale = amax / 448 in fp32 (1 if the group is all zero) and
-    code = E4M3FN(x / scale), rounded to the nearest finite value with ties to
-    the even code, saturating at 448; the row's 28 pad bytes are zero.  The
-    scale and x / scale are formed in fp32 (the precision in which the GPU
-    decides the code); the rounding to E4M3FN is exact.
+    default; the quantizer itself is not spelled out): per group of 64 the
+    scale is the smallest power of two 2^k with amax <= 448 * 2^k (k >= -126;
+    1 if the group is all zero), stored as fp32, and code = E4M3FN(x / scale),
+    rounded to the nearest finite value with ties to the even code (x / scale
+    is exact and within +-448).  Power-of-two group scales are the block
+    scales MI355X's FP8 conversion and matrix instructions apply themselves;
+    the decode above (code times scale) reads any fp32 scale.
   * Q8 prefill (LMSYS page, section 4 "Prefill dataflow optimization", and its
     configuration table: FP8 query against the FP8 KV cache for prefill; the
     query quantizer is not spelled out): one fp32 scale per query head over
@@ -344,14 +345,26 @@ def e4m3fn_encode(y) -> np.ndarray:
     return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
 
 
+def fp8_group_scale(amax) -> np.ndarray:
+    """Cache group scale: the smallest 2^k (k >= -126) with amax <= 448 * 2^k,
+    by exact comparison; 1 for amax = 0.  float32."""
+    amax = np.asarray(amax, dtype=np.float64)
+    k = np.zeros(amax.shape, dtype=np.int64)
+    for i, a in np.ndenumerate(amax):
+        if a > 0:
+            kk = -126
+            while a > 448.0 * 2.0 ** kk:
+                kk += 1
+            k[i] = kk
+    return np.ldexp(np.float32(1.0), k).astype(np.float32)
+
+
 def quantize_fp8_row(x) -> tuple[np.ndarray, np.ndarray]:
     """One 576-element row (any float input; the GPU path takes bf16) -> (codes
-    uint8[576], scales float32[9]) with scale and x / scale formed in fp32."""
-    x32 = np.asarray(x, dtype=np.float32).reshape(FP8_NGROUPS, FP8_GROUP)
-    amax = np.abs(x32).max(axis=1)
-    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    y = (x32 / scale[:, None]).astype(np.float32)
-    return e4m3fn_encode(y).reshape(D_QK), scale
+    uint8[576], scales float32[9]); x / scale is exact (a power of two)."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(FP8_NGROUPS, FP8_GROUP)
+    scale = fp8_group_scale(np.abs(x64).max(axis=1))
+    return e4m3fn_encode(x64 / scale[:, None].astype(np.float64)).reshape(D_QK), scale
 
 
 def quantize_q8(q) -> tuple[np.ndarray, np.ndarray]:

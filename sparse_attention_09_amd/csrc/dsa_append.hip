@@ -4,9 +4,12 @@
 // paged KV pool holds the latent rows - FP8 by default on MI355X - and the DSA
 // indexer pool the indexer keys.  The pages do not spell the quantizer out;
 // the reading used here (and by the oracle): per group of 64 consecutive
-// elements, scale = amax / 448 in fp32 (1 for an all-zero group) and
-// code = E4M3FN(x / scale), rounded to the nearest finite value with ties to
-// the even code and saturated at 448; the row's 28 pad bytes are written as 0.
+// elements the scale is the smallest power of two 2^k with amax <= 448 * 2^k
+// (1 for an all-zero group), stored as fp32, and code = E4M3FN(x / scale),
+// rounded to the nearest finite value with ties to the even code (x / scale
+// is exact and within +-448); the row's 28 pad bytes are written as 0.
+// Power-of-two scales are what gfx950's FP8 conversions and scaled MFMAs
+// apply in hardware, so the attention kernels never multiply by them.
 //
 // One wave per row.  Lane l holds elements 64g + l of the nine groups, so a
 // group's amax is one wave reduction and its 64 codes one coalesced 64-byte
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
       const float amax = wave_max(fabsf(v[g]));
-      scale[g] = amax > 0.f ? amax / 448.f : 1.f;
+      scale[g] = dsa::fp8_group_scale(amax);
     }
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) row[64 * g + lane] = uint8_t(dsa::e4m3_encode(v[g] / scale[g]));

@@ -76,6 +76,17 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// FP8 cache group scale: the smallest power of two 2^k (k >= -126) with
+// amax <= 448 * 2^k, 1 for amax = 0.  Exact: amax = 1.f * 2^e, and
+// 448 * 2^k = 1.75 * 2^(k+8) reaches it at k = e - 8 when f <= 1.75, else
+// at k = e - 7.
+__device__ __forceinline__ float fp8_group_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const uint32_t b = __float_as_uint(amax);
+  const int k = max(int(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0), -126);
+  return __uint_as_float(uint32_t(k + 127) << 23);
+}
+
 // Max / sum over lanes i, i^16, i^32, i^48 (the four 16-lane rows of a
 // wave), every lane receiving the result: v_permlane32_swap then
 // v_permlane16_swap each pair a lane with its partner in one VALU op (no LDS

@@ -11,9 +11,9 @@
 // One workgroup = one (token, split).  Per KV tile of TILE rows:
 //   * the selected rows are gathered through the page table in 16-byte chunks,
 //     the lanes of a wave instruction covering whole 128-byte lines; FP8 codes
-//     are dequantized in registers (exact E4M3 -> fp32, times the group scale,
-//     rounded to bf16) and written once to LDS as a row-major K tile (576
-//     wide, swizzled against bank conflicts);
+//     are dequantized in registers (the scaled FP8 -> bf16 conversion, exact
+//     for the cache's power-of-two group scales) and written once to LDS as a
+//     row-major K tile (576 wide, swizzled against bank conflicts);
 //   * the next tile's rows are prefetched into registers while the current
 //     tile is computed (gather loads are unconditional so nothing waits on them
 //     before the tile's stores);
@@ -124,13 +124,15 @@ __device__ __forceinline__ void put_lse(const PartialArgs& a, int64_t ts, int he
 template <int KV, int NR, int NT>
 struct Stage;
 
-// 4 E4M3 codes times their group scale -> 4 bf16 (two dwords): exact decode,
-// one fp32 product, round to nearest even.
+// 4 E4M3 codes times their group scale -> 4 bf16 (two dwords) with gfx950's
+// scaled conversion, two values per instruction.  It applies the exponent of
+// the fp32 scale (a block scale); the cache's group scales are powers of two,
+// so the result is the exact product (4 significant bits fit bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 dq4_bf16(uint32_t codes, float scale) {
-  float f[4];
-  dsa::fp8x4_to_f32(codes, f);
-  return u32x2{dsa::pack_bf16x2(f[0] * scale, f[1] * scale),
-               dsa::pack_bf16x2(f[2] * scale, f[3] * scale)};
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // FP8 rows: 576 codes, 9 fp32 scales at byte 576, stride 640.  Latent chunk
@@ -1084,13 +1086,14 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
 // ---------------------------------------------------------------------------
 // Q8 prefill ["Accelerating GLM-5.3-Flash on H200", section 4 "Prefill
 // dataflow optimization": the prefill attention multiplies an FP8 query with
-// the FP8 cache].  S = K Q^T runs on gfx950's 32x32x64 f8f6f4 MFMA, the FP8
-// form with twice the bf16 rate.  Its 64-deep contraction is exactly one
-// scale group of a cache row, so the product of group g's codes lands in a
-// fresh accumulator and is added into the score times that row's fp32 group
-// scale (exact up to fp32 rounding: no rescaling of codes); the query's one
-// scale per head multiplies the finished score.  The value product stays on
-// bf16 with V dequantized once per tile, as in the bf16 path.
+// the FP8 cache].  S = K Q^T runs on gfx950's scaled 32x32x64 f8f6f4 MFMA, the
+// FP8 form with twice the bf16 rate.  Its 64-deep contraction is exactly one
+// scale group of a cache row and each lane's 32 codes one block, so the
+// MFMA applies every row's power-of-two group scale itself (E8M0 block
+// scale = the exponent byte of the stored fp32 scale) and the nine group
+// products accumulate in one chain; the query's one scale per head multiplies
+// the finished score.  The value product stays on bf16 with V dequantized
+// once per tile, as in the bf16 path.
 //
 // One workgroup per token, 8 waves (wave w runs on SIMD w % 4), tiles of 32
 // rows:
@@ -1104,7 +1107,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
 //     the score waves) take 64 columns and the rope codes, so each SIMD gets a
 //     similar share of matrix and vector work.
 // Per tile the raw codes go to a ring of two buffers (score waves read tile j
-// while tile j+1 is written) with their scales beside them, the dequantized
+// while tile j+1 is written) with their scale exponents beside them, the dequantized
 // latent to a ring of three (value waves read tile j-1) and P to a ring of
 // two; one barrier per tile.
 constexpr int kTileQ8 = 32;
@@ -1129,7 +1132,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // writes conflict-free, as in the bf16 K tile.
 struct SmemQ8 {
   uint8_t k8[2][kTileQ8 * kK8Stride];          // raw E4M3 codes
-  float sc[2][kQ8Groups][kTileQ8];             // their group scales, group-major
+  uint8_t sc8[2][kTileQ8][16];                 // E8M0 exponents of the 9 group scales per row
   uint16_t v[3][kTileQ8 * kVStrideQ8];         // dequantized latent (V), bf16
   uint16_t p[2][DSA_HEADS * kPStrideWS];       // P in the PV operand's row order
   float alpha[2][DSA_HEADS];
@@ -1140,10 +1143,12 @@ struct SmemQ8 {
 };
 static_assert(sizeof(SmemQ8) <= 160 * 1024, "Q8 tiles exceed the LDS");
 
-__device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b) {
-  const f32x16 zero = {};
-  // E4M3 operands (format 0), block scales 2^0 (E8M0 127)
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+// acc += (A * 2^(ea - 127)) (B), E4M3 operands (format 0); A's block scale is
+// byte S of sa in each lane, B's is 2^0 (E8M0 127).
+template <int S>
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b, int sa,
+                                                   const f32x16& acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, S, sa, 0, 127);
 }
 
 __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
@@ -1181,7 +1186,7 @@ struct Q8Latent {
       scale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
     }
   }
-  __device__ __forceinline__ void store(uint8_t* k8, float* sc, uint16_t* v, int sid) const {
+  __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t* v, int sid) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = sid + 256 * i, r = q >> 5, c = q & 31;
@@ -1196,7 +1201,7 @@ struct Q8Latent {
       const u32x2 b0 = dq4_bf16(cd[2], s), b1 = dq4_bf16(cd[3], s);
       *reinterpret_cast<u32x4*>(v + r * kVStrideQ8 + 8 * (k_phys(2 * c) ^ 1)) =
           u32x4{b0[0], b0[1], b1[0], b1[1]};
-      if ((c & 3) == 0) sc[(c >> 2) * kTileQ8 + r] = s;
+      if ((c & 3) == 0) sc8[r * 16 + (c >> 2)] = uint8_t(__float_as_uint(s) >> 23);
     }
   }
 };
@@ -1215,25 +1220,25 @@ struct Q8Rope {
     code = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (sid & 3));
     scale = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
   }
-  __device__ __forceinline__ void store(uint8_t* k8, float* sc, uint16_t*, int sid) const {
+  __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t*, int sid) const {
     const int r = sid >> 2, c = DSA_D_LATENT / 16 + (sid & 3);
     *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) =
         ok ? code : u32x4{0, 0, 0, 0};
-    if ((sid & 3) == 0) sc[8 * kTileQ8 + r] = ok ? scale : 0.f;
+    if ((sid & 3) == 0) sc8[r * 16 + 8] = ok ? uint8_t(__float_as_uint(scale) >> 23) : 0;
   }
 };
 
 // Score waves stage nothing.
 struct Q8NoStage {
   __device__ __forceinline__ void load(const uint8_t*, const int32_t*, int) {}
-  __device__ __forceinline__ void store(uint8_t*, float*, uint16_t*, int) const {}
+  __device__ __forceinline__ void store(uint8_t*, uint8_t*, uint16_t*, int) const {}
 };
 
 // The tile loop shared by all roles (identical barriers): per chunk of
 // kRowChunkQ8 index columns the rows are resolved, tiles 0..kQ8Depth-1
 // gathered and tile 0 stored; iteration j (in whole groups of three, so the
 // gathers form one straight-line stream) calls work(j, ntile, P), stores tile
-// j + 1 (codes and scales into buffer (j + 1) % 2, V into (j + 1) % 3),
+// j + 1 (codes and scale exponents into buffer (j + 1) % 2, V into (j + 1) % 3),
 // gathers tile j + 1 + kQ8Depth and waits at the barrier.  Past the last tile
 // the row indices are clamped and the stores refill buffers nobody reads.
 template <class Stager, class Work>
@@ -1252,7 +1257,7 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
     if (ntile == 0) continue;
     auto tile_rows = [&](int i) { return sm.rows + min(i, ntile - 1) * kTileQ8; };
     dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), sid); });
-    st[0].store(sm.k8[0], &sm.sc[0][0][0], sm.v[0], sid);
+    st[0].store(sm.k8[0], &sm.sc8[0][0][0], sm.v[0], sid);
     st[0].load(a.latent, tile_rows(kD), sid);
     __syncthreads();
     for (int j0 = 0; j0 <= ntile; j0 += 3) {
@@ -1262,7 +1267,7 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
         constexpr int si = (p + 1) % kD;
         work(j, ntile, P);
         const int kn = (j + 1) & 1;
-        st[si].store(sm.k8[kn], &sm.sc[kn][0][0], sm.v[(p + 1) % 3], sid);
+        st[si].store(sm.k8[kn], &sm.sc8[kn][0][0], sm.v[(p + 1) % 3], sid);
         st[si].load(a.latent, tile_rows(j + 1 + kD), sid);
         __syncthreads();
       });
@@ -1375,32 +1380,21 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
     q8_pipeline<Q8NoStage>(a, sm, t, req, pos, tid, 0, [&](int j, int ntile, auto) {
       if (j < ntile) {
         const uint8_t* k8 = sm.k8[j & 1];
-        const float* sc = &sm.sc[j & 1][0][0];
         auto aread = [&](int g) {
           return cat8(*reinterpret_cast<const u32x4*>(k8 + ka + 64 * g),
                       *reinterpret_cast<const u32x4*>(k8 + ka + 64 * g + 32));
         };
-        // acc[4q + jj] = score of row 8q + 4h + jj: sum over groups of the
-        // group's code product times the row's group scale
-        f32x16 acc, tmp[2];
-        auto promote = [&](int g, const f32x16& pg) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 s = *reinterpret_cast<const f32x4*>(sc + g * kTileQ8 + 8 * q + 4 * h);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              acc[4 * q + jj] = g == 0 ? pg[4 * q + jj] * s[jj] : fmaf(pg[4 * q + jj], s[jj], acc[4 * q + jj]);
-          }
-        };
+        // the nine scale exponents of row m (bytes 0..8)
+        const u32x4 se = *reinterpret_cast<const u32x4*>(&sm.sc8[j & 1][n][0]);
+        // acc[4q + jj] = score of row 8q + 4h + jj over the nine groups
+        f32x16 acc = {};
         i32x8 af[2];
         af[0] = aread(0);
         dsa::static_for<kQ8Groups>([&](auto G) {
           constexpr int g = decltype(G)::value;
           if constexpr (g + 1 < kQ8Groups) af[(g + 1) & 1] = aread(g + 1);
-          tmp[g & 1] = mfma32x32x64_fp8(af[g & 1], qf[g]);
-          if constexpr (g >= 1) promote(g - 1, tmp[(g - 1) & 1]);
+          acc = mfma32x32x64_fp8<g & 3>(af[g & 1], qf[g], int(se[g >> 2]), acc);
         });
-        promote(kQ8Groups - 1, tmp[(kQ8Groups - 1) & 1]);
         // log2-domain scores (-inf on masked rows) and the tile max of the head
         float z[16];
         float tmax = kNegInf;

@@ -26,8 +26,10 @@ Value recipe: indexer queries and keys are integers drawn uniformly from
 [-8, 8] and stored as bf16; indexer head weights are integers from {1,..,4}
 (fp32); attention queries and latent rows are N(0,1).  BF16 rows are the
 round-to-nearest-even bf16 of the draws.  FP8 rows are quantized per 64
-consecutive elements: scale = amax / 448 (fp32; 1 if the group is all zero),
-code = E4M3FN(x / scale) via torch's float8_e4m3fn cast, saturated to +-448.
+consecutive elements: scale = the smallest power of two 2^k with
+amax <= 448 * 2^k (k >= -126; 1 if the group is all zero), stored as fp32,
+code = E4M3FN(x / scale) via torch's float8_e4m3fn cast (x / scale is exact
+and within +-448).
 """
 
 from __future__ import annotations
@@ -114,8 +116,12 @@ def _quantize_fp8_rows(x: torch.Tensor) -> torch.Tensor:
     n = x.shape[0]
     xg = x.view(n, 9, 64)
     amax = xg.abs().amax(dim=2)
-    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    y = (xg / scale[:, :, None]).clamp(-448.0, 448.0)
+    # amax = m * 2^e, m in [0.5, 1): 448 * 2^k >= amax first holds at
+    # k = e - 9, or e - 8 when m > 448 / 512
+    m, e = torch.frexp(amax)
+    k = torch.clamp(e - 9 + (m > 0.875).to(e.dtype), min=-126)
+    scale = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), k), torch.ones_like(amax))
+    y = xg / scale[:, :, None]
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8).view(n, 576)
     out = torch.zeros((n, 640), dtype=torch.uint8, device=x.device)
     out[:, :576] = codes

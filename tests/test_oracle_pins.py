@@ -441,28 +441,54 @@ def test_e4m3fn_encode_matches_torch_cast():
     assert np.array_equal(O.e4m3fn_encode(y), ref)
 
 
+def test_fp8_group_scale_closed_form():
+    # the smallest power of two 2^k with amax <= 448 * 2^k: 448 * 2^k itself
+    # and anything up to it take 2^k, a hair more takes 2^(k+1)
+    amax = [0.0, 448.0, 449.0, 896.0, 897.0, 1.0, 1.75, 3.0, 3.5, 3.5000002, 1e-30, 1e-40]
+    want = [1.0, 1.0, 2.0, 2.0, 4.0, 2.0 ** -8, 2.0 ** -8, 2.0 ** -7, 2.0 ** -7, 2.0 ** -6,
+            2.0 ** -108, 2.0 ** -126]
+    got = O.fp8_group_scale(np.array(amax, dtype=np.float32))
+    assert got.dtype == np.float32 and got.tolist() == want
+    # against frexp (an independent library route): amax = m * 2^e, m in
+    # [0.5, 1), the scale is 2^(e - 9), or 2^(e - 8) when m > 0.875
+    g = np.random.default_rng(15)
+    a = (g.standard_normal(20000) * 10.0 ** g.uniform(-20, 20, 20000)).astype(np.float32)
+    a = np.abs(a[a != 0])
+    m, e = np.frexp(a.astype(np.float64))
+    ref = np.ldexp(1.0, np.maximum(e - 9 + (m > 0.875), -126))
+    assert np.array_equal(O.fp8_group_scale(a).astype(np.float64), ref)
+
+
 def test_quantize_row_properties():
     g = np.random.default_rng(12)
     x = (g.standard_normal(576) * np.repeat(10.0 ** g.uniform(-3, 3, 9), 64)).astype(np.float32)
     x[64:128] = 0.0                                  # an all-zero group
     x[200] = -np.abs(x[128:192]).max() * 3           # a group dominated by one value
     codes, scales = O.quantize_fp8_row(x)
-    xg = x.reshape(9, 64)
+    xg = x.reshape(9, 64).astype(np.float64)
     amax = np.abs(xg).max(axis=1)
+    assert scales.dtype == np.float32
     assert scales[1] == np.float32(1.0) and np.all(codes[64:128] == 0)
-    want = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    assert np.array_equal(scales, want)
-    # the largest magnitude of each non-zero group encodes to +-448
     for gi in range(9):
         if amax[gi] > 0:
+            # a power of two, the smallest that brings amax within 448
+            sc = float(scales[gi])
+            assert math.frexp(sc)[0] == 0.5
+            assert amax[gi] <= 448 * sc and amax[gi] > 224 * sc
+            # nothing saturates: the largest magnitude decodes to its nearest value
             j = 64 * gi + int(np.argmax(np.abs(xg[gi])))
-            assert codes[j] & 0x7F == 0x7E
+            assert O.e4m3fn_table()[codes[j]] * sc == pytest.approx(xg.reshape(-1)[j], rel=2 ** -4)
     # dequantized error: half an E4M3 step (<= 2^-4 relative for normals,
     # 2^-10 * scale absolute in the subnormal range)
     deq = O.e4m3fn_table()[codes] * np.repeat(scales.astype(np.float64), 64)
     err = np.abs(deq - x.astype(np.float64))
     bound = np.maximum(np.abs(x) * 2.0 ** -4, np.repeat(scales.astype(np.float64), 64) * 2.0 ** -10)
     assert np.all(err <= bound * (1 + 1e-6))
+    # x / scale is exact, so the codes are the nearest E4M3 values of x / scale
+    # computed in float64, and match torch's float8 cast of the same quotient
+    y = x.astype(np.float64) / np.repeat(scales.astype(np.float64), 64)
+    ref = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
 
 
 def test_quantize_row_matches_generator_quantizer():
@@ -612,9 +638,10 @@ def test_q8_planted_mistakes_are_caught():
     each gives a code the closed-form pin above rules out."""
     q = np.zeros(576, np.float32)
     q[100], q[300] = 3.0, -1.5
-    # per-64-group scales instead of one per head: -1.5 becomes -448
+    # per-64-group scales instead of one per head: -1.5 gets its own group's
+    # scale and another code than the pinned 0xF6
     per_group, _ = O.quantize_fp8_row(q)
-    assert per_group[300] == 0xFE
+    assert per_group[300] != 0xF6
     # truncation instead of round-to-nearest-even at the midpoint 1.1875
     y = np.float32(1.1875)
     trunc = int(np.searchsorted(O.e4m3fn_table()[:0x7F], y, side="right") - 1)
