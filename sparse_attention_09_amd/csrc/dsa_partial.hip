@@ -1101,11 +1101,13 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
 //     head 32w + l%32 and rows 8q + 4(l/32) + j (q, j < 4), the query codes of
 //     its head stay in registers; online softmax with the running reference
 //     max of the bf16 kernels;
-//   * value waves: O for all 64 heads on a slice of the output columns.  Waves
-//     2, 3, 6, 7 (SIMDs 2 and 3, which hold no score wave) take 96 columns each
-//     and gather and dequantize the tile's latent codes; waves 4 and 5 (beside
-//     the score waves) take 64 columns and the rope codes, so each SIMD gets a
-//     similar share of matrix and vector work.
+//   * value waves: O for all 64 heads on a slice of the output columns; waves
+//     2, 3, 6, 7 (SIMDs 2 and 3, which hold no score wave) take 96 columns
+//     each, waves 4 and 5 (beside the score waves) 64, so each SIMD gets a
+//     similar share of matrix work;
+//   * after its role work every thread gathers and dequantizes latent chunks
+//     of the next tiles: one per thread of the wide value waves, three per
+//     thread of the others (waves 4 and 5 also the rope codes).
 // Per tile the raw codes go to a ring of two buffers (score waves read tile j
 // while tile j+1 is written) with their scale exponents beside them, the dequantized
 // latent to a ring of three (value waves read tile j-1) and P to a ring of
@@ -1167,71 +1169,68 @@ __device__ __forceinline__ float halves_sum(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Latent gather of the four wide value waves (256 threads, index sid): chunk
-// q = sid + 256i (i < 4) is row q / 32, codes 16(q % 32)..+16, group (q % 32) / 4.
-// Invalid rows load row 0 and store zero codes and scales.
-struct Q8Latent {
-  u32x4 code[4];
-  float scale[4];
+// Tile gather, spread over all 512 threads by index cid: latent chunk
+// q = cid + 256i (i < NC) is row q / 32, codes 16(q % 32)..+16, group
+// (q % 32) / 4.  The wide value waves (cid 0..255) take one chunk each, the
+// score and narrow value waves (cid 256..511) three, which keeps the wide
+// waves' registers for their accumulators and moves the vector work to the
+// waves with idle time.  With kRope the thread (waves 4 and 5, r = tid - 256)
+// also gathers rope chunk r: row r / 4, rope codes 16(r % 4)..+16, and the
+// r % 4 == 0 thread the rope group's scale.  Invalid rows load row 0 and store
+// zero codes and scales.
+template <int NC, bool kRope>
+struct Q8Stage {
+  u32x4 code[NC];
+  float scale[NC];
+  u32x4 rcode;
+  float rscale;
   uint32_t ok;
-  __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int sid) {
+  __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int cid, int tid) {
     ok = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = sid + 256 * i;
+    for (int i = 0; i < NC; ++i) {
+      const int q = cid + 256 * i;
       const int phys = rows[q >> 5];
       ok |= uint32_t(phys >= 0) << i;
       const uint8_t* row = latent + int64_t(max(phys, 0)) * 640;
       code[i] = *reinterpret_cast<const u32x4*>(row + 16 * (q & 31));
       scale[i] = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * ((q & 31) >> 2));
     }
+    if constexpr (kRope) {
+      const int r = tid - 256;
+      const int phys = rows[r >> 2];
+      ok |= uint32_t(phys >= 0) << NC;
+      const uint8_t* row = latent + int64_t(max(phys, 0)) * 640;
+      rcode = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (r & 3));
+      rscale = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
+    }
   }
-  __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t* v, int sid) const {
+  __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t* v, int cid,
+                                        int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = sid + 256 * i, r = q >> 5, c = q & 31;
+    for (int i = 0; i < NC; ++i) {
+      const int q = cid + 256 * i, r = q >> 5, c = q & 31;
       const bool okb = (ok >> i) & 1u;
       const u32x4 cd = okb ? code[i] : u32x4{0, 0, 0, 0};
       const float s = okb ? scale[i] : 0.f;
       *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) = cd;
       // bf16 chunks 2c, 2c + 1 at k_phys(2c), k_phys(2c) ^ 1
-      uint16_t* vr = v + r * kVStrideQ8 + 8 * k_phys(2 * c);
       const u32x2 a0 = dq4_bf16(cd[0], s), a1 = dq4_bf16(cd[1], s);
-      *reinterpret_cast<u32x4*>(vr) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      *reinterpret_cast<u32x4*>(v + r * kVStrideQ8 + 8 * k_phys(2 * c)) =
+          u32x4{a0[0], a0[1], a1[0], a1[1]};
       const u32x2 b0 = dq4_bf16(cd[2], s), b1 = dq4_bf16(cd[3], s);
       *reinterpret_cast<u32x4*>(v + r * kVStrideQ8 + 8 * (k_phys(2 * c) ^ 1)) =
           u32x4{b0[0], b0[1], b1[0], b1[1]};
       if ((c & 3) == 0) sc8[r * 16 + (c >> 2)] = uint8_t(__float_as_uint(s) >> 23);
     }
+    if constexpr (kRope) {
+      const int rr = tid - 256, r = rr >> 2, c = DSA_D_LATENT / 16 + (rr & 3);
+      const bool okb = (ok >> NC) & 1u;
+      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) =
+          okb ? rcode : u32x4{0, 0, 0, 0};
+      if ((rr & 3) == 0) sc8[r * 16 + 8] = okb ? uint8_t(__float_as_uint(rscale) >> 23) : 0;
+    }
   }
-};
-
-// Rope gather of the two narrow value waves (128 threads): chunk q = sid is
-// row q / 4, rope codes 16(q % 4)..+16; the q % 4 == 0 thread also writes the
-// rope group's scale.
-struct Q8Rope {
-  u32x4 code;
-  float scale;
-  bool ok;
-  __device__ __forceinline__ void load(const uint8_t* latent, const int32_t* rows, int sid) {
-    const int phys = rows[sid >> 2];
-    ok = phys >= 0;
-    const uint8_t* row = latent + int64_t(max(phys, 0)) * 640;
-    code = *reinterpret_cast<const u32x4*>(row + DSA_D_LATENT + 16 * (sid & 3));
-    scale = *reinterpret_cast<const float*>(row + DSA_D_QK + 4 * 8);
-  }
-  __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t*, int sid) const {
-    const int r = sid >> 2, c = DSA_D_LATENT / 16 + (sid & 3);
-    *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) =
-        ok ? code : u32x4{0, 0, 0, 0};
-    if ((sid & 3) == 0) sc8[r * 16 + 8] = ok ? uint8_t(__float_as_uint(scale) >> 23) : 0;
-  }
-};
-
-// Score waves stage nothing.
-struct Q8NoStage {
-  __device__ __forceinline__ void load(const uint8_t*, const int32_t*, int) {}
-  __device__ __forceinline__ void store(uint8_t*, uint8_t*, uint16_t*, int) const {}
 };
 
 // The tile loop shared by all roles (identical barriers): per chunk of
@@ -1243,7 +1242,7 @@ struct Q8NoStage {
 // the row indices are clamped and the stores refill buffers nobody reads.
 template <class Stager, class Work>
 __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, int t, int req,
-                                            int pos, int tid, int sid, Work&& work) {
+                                            int pos, int tid, int cid, Work&& work) {
   constexpr int kD = kQ8Depth;
   Stager st[kD];
   for (int cc = 0; cc < a.width; cc += kRowChunkQ8) {
@@ -1256,9 +1255,9 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
     const int ntile = (sm.last + kTileQ8) / kTileQ8;
     if (ntile == 0) continue;
     auto tile_rows = [&](int i) { return sm.rows + min(i, ntile - 1) * kTileQ8; };
-    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), sid); });
-    st[0].store(sm.k8[0], &sm.sc8[0][0][0], sm.v[0], sid);
-    st[0].load(a.latent, tile_rows(kD), sid);
+    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), cid, tid); });
+    st[0].store(sm.k8[0], &sm.sc8[0][0][0], sm.v[0], cid, tid);
+    st[0].load(a.latent, tile_rows(kD), cid, tid);
     __syncthreads();
     for (int j0 = 0; j0 <= ntile; j0 += 3) {
       dsa::static_for<3>([&](auto P) {
@@ -1267,8 +1266,8 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
         constexpr int si = (p + 1) % kD;
         work(j, ntile, P);
         const int kn = (j + 1) & 1;
-        st[si].store(sm.k8[kn], &sm.sc8[kn][0][0], sm.v[(p + 1) % 3], sid);
-        st[si].load(a.latent, tile_rows(j + 1 + kD), sid);
+        st[si].store(sm.k8[kn], &sm.sc8[kn][0][0], sm.v[(p + 1) % 3], cid, tid);
+        st[si].load(a.latent, tile_rows(j + 1 + kD), cid, tid);
         __syncthreads();
       });
     }
@@ -1279,7 +1278,7 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
 // iteration j, as in the bf16 warp-specialized kernel).
 template <int NB, class Stager>
 __device__ __forceinline__ void q8_value(const PartialArgs& a, SmemQ8& sm, int t, int req, int pos,
-                                         int tid, int sid, int d0) {
+                                         int tid, int cid, int d0) {
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   f32x4 o[4][NB];
 #pragma unroll
@@ -1293,7 +1292,7 @@ __device__ __forceinline__ void q8_value(const PartialArgs& a, SmemQ8& sm, int t
   const int vlane0 = vrow + 8 * ((c & 3) >> 1);
   const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
   const int xb = d0 >> 3;
-  q8_pipeline<Stager>(a, sm, t, req, pos, tid, sid, [&](int j, int ntile, auto P) {
+  q8_pipeline<Stager>(a, sm, t, req, pos, tid, cid, [&](int j, int ntile, auto P) {
     constexpr int p = decltype(P)::value;
     if (j >= 1 && j <= ntile) {
       const int jp = j - 1;
@@ -1377,7 +1376,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
     const int ka = n * kK8Stride + 16 * (h ^ ((n >> 4) & 1));
     const int sw = p_swz(head & 15);
     float m_run = kNegInf, l_run = 0.f;
-    q8_pipeline<Q8NoStage>(a, sm, t, req, pos, tid, 0, [&](int j, int ntile, auto) {
+    q8_pipeline<Q8Stage<3, false>>(a, sm, t, req, pos, tid, 256 + tid, [&](int j, int ntile, auto) {
       if (j < ntile) {
         const uint8_t* k8 = sm.k8[j & 1];
         auto aread = [&](int g) {
@@ -1440,11 +1439,11 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
     }
     __syncthreads();
   } else if (wave == 4 || wave == 5) {
-    q8_value<4, Q8Rope>(a, sm, t, req, pos, tid, tid - 256, 192 + 64 * (wave - 4));
+    q8_value<4, Q8Stage<3, true>>(a, sm, t, req, pos, tid, tid + 128, 192 + 64 * (wave - 4));
   } else {
     const int hw = wave < 4 ? wave - 2 : wave - 4;   // waves 2, 3, 6, 7 -> 0..3
     const int d0 = hw < 2 ? 96 * hw : 320 + 96 * (hw - 2);
-    q8_value<6, Q8Latent>(a, sm, t, req, pos, tid, 64 * hw + lane, d0);
+    q8_value<6, Q8Stage<1, false>>(a, sm, t, req, pos, tid, 64 * hw + lane, d0);
   }
 }
 
