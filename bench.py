@@ -4,7 +4,7 @@ One step = the whole path over one batch: indexer scores -> top-k (fused into
 one call without a score matrix for rows up to 65,536) -> sparse MLA partial
 -> combine, with inputs resident in HBM.  Default workload: the
 speculative-verify decode batch, 128 requests x 8 query tokens, 64K context
-each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
+each, FP8 E4M3 latent KV (per-64 power-of-two scales) in 64-token pages, top-2048,
 64 heads.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -13,7 +13,8 @@ each, FP8 E4M3 latent KV (per-64 fp32 scales) in 64-token pages, top-2048,
   python bench.py --summarize-mfma COUNTER_CSV WORKLOAD CMD...        (MFMA-use JSON)
 
 With no flags the line also carries the 32K-token prefill chunk (Partial
-against the bf16 MFMA peak), the shared-prefix batch at KV tiles 32 / 64 /
+against the bf16 MFMA peak, and the Q8 variant: FP8 query quantizer + Q8
+attention on the same rows), the shared-prefix batch at KV tiles 32 / 64 /
 128, and the box's measured copy bandwidth and bf16 GEMM rate.
 """
 
@@ -30,6 +31,7 @@ import torch
 METRIC = "sparse-MLA query tokens/s + HBM GB/s % peak, 64K ctx top-2048, 64 heads"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, vendor figure
 
 
 def algorithmic_bytes(spec, plan, kv_row_bytes, fused=False):
@@ -490,10 +492,45 @@ def bench_prefill(dsa, synth, dev, cus, flush, peaks, steps=5, warmup=2):
                         "flops_per_launch": int(fl["partial"]),
                         "counters": mfma_counters(spec.name, "partial")},
            "fallback_tokens": path.fallback_count()}
+    out["q8"] = bench_q8(dsa, spec, wl, pool, path, stream, flush, steps, fl["partial"])
     pool.close()
     del wl, path, pool
     torch.cuda.empty_cache()
     return out
+
+
+def bench_q8(dsa, spec, wl, pool, path, stream, flush, steps, flops_partial):
+    """Q8 on the same chunk and the same selected rows: the query quantizer and
+    the Q8 attention (FP8 query x FP8 rows on the f8f6f4 MFMA, bf16 PV).  The
+    roof of the attention is its mixed peak: the score's FLOPs at the FP8
+    peak plus the value product's at the bf16 peak."""
+    import statistics
+    T = spec.num_tokens
+    codes = torch.empty((T, 64, 576), dtype=torch.uint8, device=wl.q.device)
+    scales = torch.empty((T, 64), dtype=torch.float32, device=wl.q.device)
+    out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=wl.q.device)
+    lse = torch.empty((T, 64), dtype=torch.float32, device=wl.q.device)
+    calls = [lambda: dsa.quantize_q8(wl.q, codes, scales),
+             lambda: dsa.sparse_mla_q8(pool, wl.page_table, wl.q_offsets, wl.tok_pos, codes, scales,
+                                       path.idx, spec.sm_scale, out, lse)]
+    names = ["quantize_q8", "partial_q8"]
+    for _ in range(2):
+        for c in calls:
+            c()
+    step_ms, per_us = time_steps(calls, names, steps, stream, flush)
+    qk = T * 64 * spec.k * 576 * 2
+    pv = T * 64 * spec.k * 512 * 2
+    mixed_peak = (qk + pv) / (qk / FP8_PEAK_TFLOPS + pv / BF16_PEAK_TFLOPS)
+    tf = flops_partial / (per_us["partial_q8"] * 1e-6) / 1e12
+    qbytes = T * 64 * (576 * 2 + 576 + 4)
+    return {"ms_per_step": round(statistics.median(step_ms), 3),
+            "quantize_q8": {"avg_us": round(per_us["quantize_q8"], 1),
+                            "gbps": round(qbytes / (per_us["quantize_q8"] * 1e-6) / 1e9, 1)},
+            "partial_q8": {"avg_us": round(per_us["partial_q8"], 1), "tflops": round(tf, 1),
+                           "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                           "mixed_peak_tflops": round(mixed_peak, 1),
+                           "frac_of_mixed_peak": round(tf / mixed_peak, 4)},
+            "note": "same selected rows as the bf16 Partial above; FLOPs counted as for it"}
 
 
 def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=10, warmup=3, tiles=(32, 64, 128)):

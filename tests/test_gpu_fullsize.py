@@ -158,3 +158,34 @@ def test_fused_select_full(name):
     _check_tokens(wl, path, out, lse, _sample(wl.num_tokens, 3, 4))
     del wl, path, out, lse, idx_fused
     torch.cuda.empty_cache()
+
+
+def test_prefill_fp8_32k_q8_full():
+    """The Q8 path on the 32K prefill chunk in the benchmark's configuration
+    (the fused selection's rows, the FP8 query quantizer, the Q8 attention):
+    every token finite and within the FP8-query distance of the bf16-query
+    output, sampled tokens against the oracle (query codes bit for bit,
+    attention within tolerance)."""
+    from oracle import dsa_oracle as O
+    wl = _gen("prefill_fp8_32k")
+    path, out16, _ = _run(wl, select="auto")
+    codes, scales = dsa.quantize_q8(wl.q)
+    out, lse = dsa.sparse_mla_q8(path.pool, wl.page_table, wl.q_offsets, wl.tok_pos, codes, scales,
+                                 path.idx, wl.spec.sm_scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    assert float((out.float() - out16.float()).abs().max()) < 0.1
+    tokens = _sample(wl.num_tokens, 3, 5)
+    reqs = sorted(set(int(wl.tok_req[t]) for t in tokens))
+    say(f"[case] prefill Q8: oracle on tokens {tokens}")
+    hv = HostView(wl, reqs=reqs)
+    for t in tokens:
+        rc, rs = O.quantize_q8(O.bf16_bits_to_f64(hv.q[t]))
+        assert np.array_equal(codes[t].cpu().numpy(), rc) and np.array_equal(scales[t].cpu().numpy(), rs)
+        b, pos = int(hv.tok_req[t]), int(hv.tok_pos[t])
+        ref = O.token_path_q8(hv.pool, hv.pt[b], pos, path.idx[t].cpu().numpy(), rc, rs,
+                              wl.spec.sm_scale)
+        check_attention(bf16_to_f64(out[t]), lse[t].cpu().numpy().astype(np.float64), ref["o"],
+                        ref["lse"], f"Q8 token {t}")
+    del wl, path, out16, out, lse, codes, scales
+    torch.cuda.empty_cache()
