@@ -832,6 +832,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
 // dequantized and stored to LDS once, in small steps placed between the QK
 // MFMAs so that the VALU and LDS work runs beside the matrix pipe.
 constexpr int kTileWS = 32;
+constexpr int kWSValueWaves = 8;            // value waves (4: 128 columns each, 8: 64)
 constexpr int kWSKLook = 2;                 // k-steps ahead the score waves read K fragments
 constexpr int kPStrideWS = kTileWS;         // bf16 per head in a P buffer (64 bytes)
 
@@ -851,8 +852,18 @@ struct SmemWS {
   int last;
 };
 
-template <int KV>
-constexpr int ws_depth() { return KV == DSA_KV_FP8_E4M3_S64 ? 3 : 1; }
+// Tiles gathered ahead into registers: 3 for FP8 rows in the 8-wave form; 1
+// for BF16 rows (twice the bytes) and in the 12-wave form, whose 168-register
+// budget holds one staged tile beside the accumulators (three spilled inside
+// the tile loop and ran 15% slower).
+template <int KV, int NV>
+constexpr int ws_depth() { return KV == DSA_KV_FP8_E4M3_S64 && NV == 4 ? 3 : 1; }
+
+// Waves that stage nothing (the score waves of the 12-wave form).
+struct NoStage {
+  __device__ __forceinline__ void load(const uint8_t*, const int32_t*, int) {}
+  __device__ __forceinline__ void store(uint16_t*, int, int) const {}
+};
 
 
 // The tile pipeline shared by both roles, so that both execute exactly the
@@ -866,25 +877,27 @@ constexpr int ws_depth() { return KV == DSA_KV_FP8_E4M3_S64 ? 3 : 1; }
 // the kernel measured slower.  Loads and stores run unconditionally (row
 // indices clamped to the chunk's last tile): past the last tile they refill
 // a buffer nobody reads.
-template <int KV, class Work>
+template <int KV, int NV, class Stager, class Work>
 __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, int t, int req,
-                                            int pos, int c0, int c1, int tid, Work&& work) {
+                                            int pos, int c0, int c1, int tid, int sid,
+                                            Work&& work) {
   constexpr int TILE = kTileWS;
-  constexpr int kD = ws_depth<KV>();
-  Stage<KV, TILE, kThreadsV2> st[kD];
+  constexpr int NT = (4 + NV) * 64;
+  constexpr int kD = ws_depth<KV, NV>();
+  Stager st[kD];
   for (int cc = c0; cc < c1; cc += kRowChunk) {
     const int cend = min(c1, cc + kRowChunk);
     __syncthreads();                            // every thread has read the last chunk's state
     if (tid == 0) sm.last = -1;
     __syncthreads();
-    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
+    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, NT, &sm.last, sm.bias);
     __syncthreads();
     const int ntile = (sm.last + TILE) / TILE;
     if (ntile == 0) continue;
     auto tile_rows = [&](int i) { return sm.rows + min(i, ntile - 1) * TILE; };
-    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), tid); });
-    st[0].store(sm.k[0], 0, tid);
-    st[0].load(a.latent, tile_rows(kD), tid);
+    dsa::static_for<kD>([&](auto D) { st[decltype(D)::value].load(a.latent, tile_rows(D), sid); });
+    st[0].store(sm.k[0], 0, sid);
+    st[0].load(a.latent, tile_rows(kD), sid);
     __syncthreads();
     // Whole groups of three iterations, every one staging and fetching: the
     // fetches then form one straight-line stream whose in-order completion
@@ -896,20 +909,27 @@ __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, in
         const int j = j0 + p;
         constexpr int si = (p + 1) % kD;
         work(j, ntile, P);
-        st[si].store(sm.k[(p + 1) % 3], 0, tid);
-        st[si].load(a.latent, tile_rows(j + 1 + kD), tid);
+        st[si].store(sm.k[(p + 1) % 3], 0, sid);
+        st[si].load(a.latent, tile_rows(j + 1 + kD), sid);
         __syncthreads();
       });
     }
   }
 }
 
-template <int KV, bool kFinal>
-__global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
+template <int KV, bool kFinal, int NV>
+__global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) SmemWS sm;
   constexpr int TILE = kTileWS;
+  // 4 value waves: every thread stages (Stage over 512 threads); 8: the score
+  // waves hold the Q of their heads and stage nothing, the 512 value threads
+  // stage the whole tile
+  using ScoreStage = std::conditional_t<NV == 4, Stage<KV, TILE, 512>, NoStage>;
+  using ValueStage = Stage<KV, TILE, 512>;
+  constexpr int kSidValue0 = NV == 4 ? 256 : 0;   // stage index of the first value thread
   constexpr int kQS = DSA_D_QK / 32;           // 18 QK k-steps
-  constexpr int kNB = DSA_D_LATENT / 64;       // 8 column blocks of a value wave
+  constexpr int kNB = DSA_D_LATENT / (16 * NV);   // 16-column blocks of a value wave
+  constexpr int kVCols = DSA_D_LATENT / NV;        // output columns of a value wave
 
   const int t = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -935,7 +955,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
     // 4ks + (g ^ bit1(ks))
     const int klane0 = c * kKStride + 8 * g;
     const int klane1 = c * kKStride + 8 * (g ^ 1);
-    ws_pipeline<KV>(a, sm, t, req, pos, c0, c1, tid, [&](int j, int ntile, auto P) {
+    ws_pipeline<KV, NV, ScoreStage>(a, sm, t, req, pos, c0, c1, tid, tid, [&](int j, int ntile, auto P) {
       constexpr int p = decltype(P)::value;
       if (j < ntile) {
         const uint16_t* kq0 = sm.k[p] + klane0;
@@ -1009,19 +1029,21 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
     }
     __syncthreads();
   } else {
-    // ---- value wave: all 64 heads, output columns 128q..+128
+    // ---- value wave: all 64 heads, output columns kVCols*q..+kVCols
     const int q = wave - 4;
     f32x4 o[4][kNB];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // V transpose read: rows 4g + c/4 (+16), columns 128q + 16nb
-    // logical chunk 16q + 2nb + (c%4)/2, bit 3 = bit 2 of nb selects the base
-    const int vrow = (4 * g + (c >> 2)) * kKStride + (DSA_D_LATENT / 4) * q + 4 * (c & 1);
+    // V transpose read: rows 4g + c/4 (+16), columns kVCols*q + 16nb: logical
+    // chunk x = (kVCols/8)q + 2nb + (c%4)/2; bit 3 of the even chunk (the same
+    // for the whole wave) selects the lane base
+    const int vrow = (4 * g + (c >> 2)) * kKStride + kVCols * q + 4 * (c & 1);
     const int vlane0 = vrow + 8 * ((c & 3) >> 1);
     const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
-    ws_pipeline<KV>(a, sm, t, req, pos, c0, c1, tid, [&](int j, int ntile, auto P) {
+    ws_pipeline<KV, NV, ValueStage>(a, sm, t, req, pos, c0, c1, tid, tid - 256 + kSidValue0,
+                                    [&](int j, int ntile, auto P) {
       constexpr int p = decltype(P)::value;
       if (j >= 1 && j <= ntile) {
         const int jp = j - 1;   // PV of the previous tile, in K buffer (p + 2) % 3
@@ -1051,7 +1073,8 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
         // next tile after each block's four MFMAs
         const uint16_t* vt = sm.k[(p + 2) % 3];
         auto vread = [&](int nb) {
-          const uint16_t* vp = vt + ((nb >> 2) & 1 ? vlane1 : vlane0) + 16 * nb;
+          const int x = (kVCols / 8) * q + 2 * nb;
+          const uint16_t* vp = vt + ((x >> 3) & 1 ? vlane1 : vlane0) + 16 * nb;
           const u32x2 lo2 = lds_read_tr16(vp);
           const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -1078,7 +1101,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_ws_kernel(PartialArgs a) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          put_out<kFinal>(a, ts, hh, (DSA_D_LATENT / 4) * q + 16 * nb + c, o[hb][nb][jj] * inv);
+          put_out<kFinal>(a, ts, hh, kVCols * q + 16 * nb + c, o[hb][nb][jj] * inv);
       }
   }
 }
@@ -1452,7 +1475,8 @@ hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
   if constexpr (TILE == kTile4)
     hipLaunchKernelGGL((partial4_kernel<KV, kFinal>), dim3(T, S), dim3(kThreads4), 0, st, a);
   else if constexpr (TILE == kTileWS)
-    hipLaunchKernelGGL((partial_ws_kernel<KV, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
+    hipLaunchKernelGGL((partial_ws_kernel<KV, kFinal, kWSValueWaves>), dim3(T, S),
+                       dim3((4 + kWSValueWaves) * 64), 0, st, a);
   else
     hipLaunchKernelGGL((partial_v2_kernel<KV, TILE, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   return hipGetLastError();
