@@ -1128,9 +1128,8 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
 //     2, 3, 6, 7 (SIMDs 2 and 3, which hold no score wave) take 96 columns
 //     each, waves 4 and 5 (beside the score waves) 64, so each SIMD gets a
 //     similar share of matrix work;
-//   * after its role work every thread gathers and dequantizes latent chunks
-//     of the next tiles: one per thread of the wide value waves, three per
-//     thread of the others (waves 4 and 5 also the rope codes).
+//   * after its role work every thread gathers and dequantizes two latent
+//     chunks of a coming tile (waves 4 and 5 also the rope codes).
 // Per tile the raw codes go to a ring of two buffers (score waves read tile j
 // while tile j+1 is written) with their scale exponents beside them, the dequantized
 // latent to a ring of three (value waves read tile j-1) and P to a ring of
@@ -1140,7 +1139,6 @@ constexpr int kRowChunkQ8 = 1024;              // index columns resolved at once
 constexpr int kK8Stride = DSA_D_QK + 16;       // bytes per raw-code row: 37 16-byte chunks
 constexpr int kVStrideQ8 = DSA_D_LATENT + 16;  // bf16 per V row: 1056 bytes = 33 x 32
 constexpr int kQ8Groups = DSA_D_QK / 64;       // 9 scale groups = 9 MFMA k-steps
-constexpr int kQ8Depth = 3;                    // tiles gathered ahead into registers
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -1192,17 +1190,18 @@ __device__ __forceinline__ float halves_sum(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Tile gather, spread over all 512 threads by index cid: latent chunk
+// Tile gather, spread over all 512 threads by chunk index cid: latent chunk
 // q = cid + 256i (i < NC) is row q / 32, codes 16(q % 32)..+16, group
-// (q % 32) / 4.  The wide value waves (cid 0..255) take one chunk each, the
-// score and narrow value waves (cid 256..511) three, which keeps the wide
-// waves' registers for their accumulators and moves the vector work to the
-// waves with idle time.  With kRope the thread (waves 4 and 5, r = tid - 256)
-// also gathers rope chunk r: row r / 4, rope codes 16(r % 4)..+16, and the
-// r % 4 == 0 thread the rope group's scale.  Invalid rows load row 0 and store
-// zero codes and scales.
-template <int NC, bool kRope>
+// (q % 32) / 4.  Every thread takes two chunks; the wide value waves (cid
+// 0..511), whose registers hold the 96-column accumulators, gather one tile
+// ahead, the score and narrow value waves three (measured 3% faster than
+// loading the wide waves less).  With kRope the thread (waves 4 and 5,
+// r = tid - 256) also gathers rope chunk r: row r / 4, rope codes
+// 16(r % 4)..+16, and the r % 4 == 0 thread the rope group's scale.  Invalid
+// rows load row 0 and store zero codes and scales.
+template <int NC, bool kRope, int kDepthT>
 struct Q8Stage {
+  static constexpr int kDepth = kDepthT;     // tiles gathered ahead (1 or 3)
   u32x4 code[NC];
   float scale[NC];
   u32x4 rcode;
@@ -1257,16 +1256,18 @@ struct Q8Stage {
 };
 
 // The tile loop shared by all roles (identical barriers): per chunk of
-// kRowChunkQ8 index columns the rows are resolved, tiles 0..kQ8Depth-1
+// kRowChunkQ8 index columns the rows are resolved, tiles 0..kD-1
 // gathered and tile 0 stored; iteration j (in whole groups of three, so the
 // gathers form one straight-line stream) calls work(j, ntile, P), stores tile
 // j + 1 (codes and scale exponents into buffer (j + 1) % 2, V into (j + 1) % 3),
-// gathers tile j + 1 + kQ8Depth and waits at the barrier.  Past the last tile
+// gathers tile j + 1 + kD and waits at the barrier (kD = the role's
+// Stager::kDepth, 1 or 3, so a role's register stages divide the group of
+// three iterations).  Past the last tile
 // the row indices are clamped and the stores refill buffers nobody reads.
 template <class Stager, class Work>
 __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, int t, int req,
                                             int pos, int tid, int cid, Work&& work) {
-  constexpr int kD = kQ8Depth;
+  constexpr int kD = Stager::kDepth;
   Stager st[kD];
   for (int cc = 0; cc < a.width; cc += kRowChunkQ8) {
     const int cend = min(a.width, cc + kRowChunkQ8);
@@ -1399,7 +1400,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
     const int ka = n * kK8Stride + 16 * (h ^ ((n >> 4) & 1));
     const int sw = p_swz(head & 15);
     float m_run = kNegInf, l_run = 0.f;
-    q8_pipeline<Q8Stage<3, false>>(a, sm, t, req, pos, tid, 256 + tid, [&](int j, int ntile, auto) {
+    q8_pipeline<Q8Stage<2, false, 3>>(a, sm, t, req, pos, tid, 512 + tid, [&](int j, int ntile, auto) {
       if (j < ntile) {
         const uint8_t* k8 = sm.k8[j & 1];
         auto aread = [&](int g) {
@@ -1462,11 +1463,11 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
     }
     __syncthreads();
   } else if (wave == 4 || wave == 5) {
-    q8_value<4, Q8Stage<3, true>>(a, sm, t, req, pos, tid, tid + 128, 192 + 64 * (wave - 4));
+    q8_value<4, Q8Stage<2, true, 3>>(a, sm, t, req, pos, tid, tid + 384, 192 + 64 * (wave - 4));
   } else {
     const int hw = wave < 4 ? wave - 2 : wave - 4;   // waves 2, 3, 6, 7 -> 0..3
     const int d0 = hw < 2 ? 96 * hw : 320 + 96 * (hw - 2);
-    q8_value<6, Q8Stage<1, false>>(a, sm, t, req, pos, tid, 64 * hw + lane, d0);
+    q8_value<6, Q8Stage<2, false, 1>>(a, sm, t, req, pos, tid, 64 * hw + lane, d0);
   }
 }
 
