@@ -187,11 +187,13 @@ KERNEL_PATTERNS = [
     ("index_scores", r"index_kernel(ILi0E|<0>)"), ("index_sample", r"index_kernel(ILi1E|<1>)"),
     ("index_emit", r"index_kernel(ILi2E|<2>)"), ("threshold", r"threshold_kernel"),
     ("select", r"select_kernel"), ("fallback", r"fallback_kernel"), ("topk", r"topk_kernel"),
+    ("partial_q8", r"partial_q8_kernel"), ("quantize_q8", r"quantize_q8_kernel"),
     ("partial", r"partial"), ("combine", r"combine_kernel")]
 FUSED_SELECT = ("index_sample", "threshold", "index_emit", "select", "fallback")
 KERNEL_SOURCES = {"index_scores": ("dsa_index.hip",), "topk": ("dsa_topk.hip",),
                   "index_topk": ("dsa_index.hip", "dsa_topk.hip"),
                   "partial": ("dsa_partial.hip",), "combine": ("dsa_partial.hip",),
+                  "partial_q8": ("dsa_partial.hip",), "quantize_q8": ("dsa_append.hip",),
                   "dcp_merge": ("dsa_topk.hip",)}
 for _k in FUSED_SELECT:
     KERNEL_SOURCES[_k] = KERNEL_SOURCES["index_topk"]
@@ -286,13 +288,17 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands: list)
     return out
 
 
+MOPS_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+
+
 def summarize_mfma(csv_path: str, workload: str, commands: list) -> dict:
     """Matrix-core use of each path kernel from a rocprofv3 counter run with
-    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 FLOPs), SQ_VALU_MFMA_BUSY_CYCLES
-    (summed over SIMDs), GRBM_GUI_ACTIVE (summed over the 8 XCDs) and,
-    optionally, the derived MfmaUtil (per cent).  Per launch: the counted
-    bf16 MFMA TFLOP/s over the dispatch's own duration, and the share of SIMD
-    cycles the matrix pipe was busy."""
+    SQ_INSTS_VALU_MFMA_MOPS_{BF16,F8,F6F4} (units of 512 FLOPs; those the run
+    collected), SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs), GRBM_GUI_ACTIVE
+    (summed over the 8 XCDs) and, optionally, the derived MfmaUtil (per cent).
+    Per launch: the counted MFMA TFLOP/s over the dispatch's own duration (per
+    type and in total), and the share of SIMD cycles the matrix pipe was busy."""
     import csv
     import statistics
     per = {}
@@ -305,18 +311,22 @@ def summarize_mfma(csv_path: str, workload: str, commands: list) -> dict:
         d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
     simds = 256 * 4
     out = {"workload": workload, "commands": commands,
-           "counters": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs; SQ_VALU_MFMA_BUSY_CYCLES / "
+           "counters": "SQ_INSTS_VALU_MFMA_MOPS_{BF16,F8,F6F4} x 512 FLOPs; SQ_VALU_MFMA_BUSY_CYCLES / "
                        "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); MfmaUtil as rocprofv3 derives it",
            "kernels": {}}
     for k, ds in per.items():
         rows = list(ds.values())
         e = {"dispatches": len(rows), "source_sha": source_sha(k)}
-        mops = [r["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for r in rows if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in r]
-        ns = [r["_ns"] for r in rows if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in r]
-        if mops:
+        have = [c for c in MOPS_COUNTERS if any(c in r for r in rows)]
+        if have:
+            mops = [sum(r.get(c, 0.0) for c in have) for r in rows]
+            ns = [r["_ns"] for r in rows]
             e["mfma_tflops_counted"] = round(statistics.median(
                 m * 512 / (t * 1e-9) / 1e12 for m, t in zip(mops, ns)), 1)
             e["mfma_flops_counted"] = int(statistics.median(m * 512 for m in mops))
+            if len(have) > 1:
+                e["mfma_flops_by_type"] = {c.rsplit("_", 1)[1]: int(statistics.median(
+                    r.get(c, 0.0) * 512 for r in rows)) for c in have}
         busy = [r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] / 8 * simds)
                 for r in rows if "SQ_VALU_MFMA_BUSY_CYCLES" in r and r.get("GRBM_GUI_ACTIVE")]
         if busy:
@@ -609,6 +619,9 @@ def main():
                     help="time back-to-back steps without the cache flush between them")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the prefill and shared-prefix entries and the measured peaks")
+    ap.add_argument("--q8", action="store_true",
+                    help="also time the Q8 variant (query quantizer + Q8 attention) on the "
+                         "workload's selected rows (FP8 pools)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB read + 1 GiB write elementwise copy "
                          "(reference dispatch for HBM byte counters)")
@@ -743,6 +756,8 @@ def main():
     if path.fused_topk:
         result["fused_select"] = {"fallback_tokens": fallback_tokens, "cap": path.cap,
                                   "unfused_us": unfused}
+    if args.q8 and spec.kv_dtype == dsa.KV_FP8:
+        result["q8"] = bench_q8(dsa, spec, wl, pool, path, stream, flush, args.steps, fl["partial"])
     result["kv_append"] = time_kv_append(dsa, spec.kv_dtype, dev)
     if not args.no_dcp and spec.num_tokens * spec.k <= (1 << 22):
         print("[bench] DCP shard layout", file=sys.stderr, flush=True)
