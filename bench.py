@@ -470,7 +470,8 @@ def mfma_counters(workload: str, kernel: str):
     d = json.load(open(path)).get("kernels", {}).get(kernel)
     if not d or d.get("source_sha") != source_sha(kernel):
         return None
-    return {k: d[k] for k in ("mfma_util", "mfma_tflops_counted", "busy_cycles_frac") if k in d}
+    return {k: d[k] for k in ("mfma_util", "mfma_tflops_counted", "busy_cycles_frac",
+                              "mfma_flops_by_type") if k in d}
 
 
 def bench_prefill(dsa, synth, dev, cus, flush, peaks, steps=5, warmup=2):
@@ -539,7 +540,8 @@ def bench_q8(dsa, spec, wl, pool, path, stream, flush, steps, flops_partial):
             "partial_q8": {"avg_us": round(per_us["partial_q8"], 1), "tflops": round(tf, 1),
                            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                            "mixed_peak_tflops": round(mixed_peak, 1),
-                           "frac_of_mixed_peak": round(tf / mixed_peak, 4)},
+                           "frac_of_mixed_peak": round(tf / mixed_peak, 4),
+                           "counters": mfma_counters(spec.name, "partial_q8")},
             "note": "same selected rows as the bf16 Partial above; FLOPs counted as for it"}
 
 
