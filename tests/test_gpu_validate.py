@@ -55,6 +55,7 @@ def test_validate_rejects_corrupt_batch(validate, what):
         lambda: dsa.index_topk(pool, pt, qo, tp, wl.q_idx, wl.w, wl.max_q, wl.max_ctx, wl.spec.k),
         lambda: dsa.sparse_mla(pool, pt, qo, tp, wl.q, idx, wl.spec.sm_scale, 64),
         lambda: dsa.sparse_mla_partial(pool, pt, qo, tp, wl.q, idx, wl.spec.sm_scale, 32, 2),
+        lambda: dsa.sparse_mla_q8(pool, pt, qo, tp, *dsa.quantize_q8(wl.q), idx, wl.spec.sm_scale),
     ]
     for call in calls:
         with pytest.raises(dsa.DsaError) as e:
