@@ -241,7 +241,9 @@ dsa_status dsa_index_topk(const dsa_pool* pool, const int32_t* page_table, int32
 
 /* Dispatch plan of the Partial step [LMSYS-3 and Figure 4].  Host-only.
  *   kv_tile: 32, 64 or 128 KV entries per loop iteration, or 0 = choose
- *   (32 when num_tokens >= cu_count or width < 1024, else 64).
+ *   (32 when num_tokens >= cu_count or width < 1024, else 64).  Splits are
+ *   cut at multiples of the tile; tiles of 32 and 128 run the same kernel,
+ *   which moves rows through LDS 32 at a time.
  *   num_splits: KV splits per token, or 0 = choose from query parallelism
  *   (num_tokens) and cu_count (0 = 256, MI355X): 1 when num_tokens >=
  *   cu_count, else about one workgroup per CU with at least two tiles per

@@ -87,6 +87,15 @@ __device__ __forceinline__ float fp8_group_scale(float amax) {
   return __uint_as_float(uint32_t(k + 127) << 23);
 }
 
+// Lane index (0..63) computed where it is called.  The asm is volatile, so
+// two calls are never merged: a value derived from it is recomputed in a loop
+// body instead of being held in a register through the loop.
+__device__ __forceinline__ int fresh_lane() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
 // Max / sum over lanes i, i^16, i^32, i^48 (the four 16-lane rows of a
 // wave), every lane receiving the result: v_permlane32_swap then
 // v_permlane16_swap each pair a lane with its partner in one VALU op (no LDS

@@ -21,13 +21,16 @@
 //     the whole split; O += P V reads V = K[:, :512] from the same LDS tile with
 //     the gfx950 transpose read (ds_read_b64_tr_b16), so no transposed copy is
 //     made.
-// Two layouts:
-//   * tiles of 32 and 64 rows (partial_v2_kernel): 8 waves, 2 per SIMD, each
-//     owning 32 heads, with a softmax whose per-head reference is fixed once
-//     (described at the kernel);
-//   * tiles of 128 rows (the K tile alone takes 148 KB of LDS): 4 waves, wave
-//     w owns heads 16w..+16 for all dims and columns, with a running reference
-//     max that rescales O only when it grows by more than 2^8.
+// Kernels:
+//   * tiles of 32 and 128 index columns (partial_ws_kernel): 12 waves in a
+//     score role and a value role one 32-row tile apart, a running reference
+//     max that rescales O only when it grows by more than 2^8 (described at
+//     the kernel); a 128-column tile is four of its 32-row LDS steps;
+//   * tiles of 64 (partial_v2_kernel, split batches): 8 waves, 2 per SIMD,
+//     each owning 32 heads, with a softmax whose per-head reference is fixed
+//     once (described at the kernel);
+//   * the Q8 variant (partial_q8_kernel): FP8 query codes against the raw FP8
+//     rows on the scaled f8f6f4 MFMA.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -345,226 +348,6 @@ __device__ __forceinline__ int request_of(const PartialArgs& a, int t) {
   return lo;
 }
 
-// Online softmax of one tile for the 16 heads of a wave (lane holds rows
-// 16mb + 4g + j of head c, log2-domain scores or -inf when masked).  Updates
-// the reference max (rescaling O when it moves), the running sum, and returns
-// P as the PV A operand.
-template <int kMB, int kNB>
-__device__ __forceinline__ void softmax_tile(f32x4 (&sacc)[kMB], f32x4 (&o)[kNB], float& m_ref,
-                                             float& l_run, u32x4 (&pa)[kMB / 2], int g) {
-  float tmax = kNegInf;
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sacc[mb][j]);
-  tmax = dsa::rows4_max(tmax);
-  if (__any(tmax > m_ref + kRescaleThreshold)) {
-    const float m_new = fmaxf(m_ref, tmax);
-    const float alpha = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-    l_run *= alpha;
-    m_ref = m_new;
-    float aj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[nb][j] *= aj[j];
-  }
-  float psum = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // masked rows carry -inf; m_ref is finite whenever a row is valid
-      // v_exp_f32: arguments are <= 8, results flush to 0 far below the max
-      p[j] = sacc[mb][j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sacc[mb][j] - m_ref);
-      psum += p[j];
-    }
-    const int k2 = mb >> 1, half = (mb & 1) * 2;
-    pa[k2][half] = dsa::pack_bf16x2(p[0], p[1]);
-    pa[k2][half + 1] = dsa::pack_bf16x2(p[2], p[3]);
-  }
-  psum = dsa::rows4_sum(psum);
-  l_run += psum;
-}
-
-// O[16 heads x kNB*16 columns from column col0] += P V over kKS*32 rows, V read
-// transposed from the K tile.
-template <int kKS, int kNB>
-__device__ __forceinline__ void pv_tile(const uint16_t* k, const u32x4 (&pa)[kKS], f32x4 (&o)[kNB],
-                                        int col0, int g, int c) {
-  // lane reads rows 32k2 + 4g + c/4 (+16), columns col0 + 16nb + 4(c%4) .. +4:
-  // logical chunk col0/8 + 2nb + (c%4)/2, whose bit 3 (bit 2 of nb when col0
-  // is a multiple of 128) selects the lane base
-  const int vrow = (4 * g + (c >> 2)) * kKStride + col0 + 4 * (c & 1);
-  const uint16_t* vbase0 = k + vrow + 8 * ((c & 3) >> 1);
-  const uint16_t* vbase1 = k + vrow + 8 * (((c & 3) >> 1) ^ 1);
-  // two column blocks in flight, their MFMAs alternating
-#pragma unroll
-  for (int nb = 0; nb < kNB; nb += 2) {
-    u32x4 vb[2][kKS];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int k2 = 0; k2 < kKS; ++k2) {
-        const uint16_t* vp = (((nb + e) >> 2) & 1 ? vbase1 : vbase0) + 32 * k2 * kKStride + 16 * (nb + e);
-        const u32x2 lo2 = lds_read_tr16(vp);
-        const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
-        vb[e][k2] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-      }
-#pragma unroll
-    for (int k2 = 0; k2 < kKS; ++k2)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        o[nb + e] = dsa::mfma16x16x32(dsa::as_bf16x8(pa[k2]), dsa::as_bf16x8(vb[e][k2]), o[nb + e]);
-  }
-}
-
-// Scales S^T into the log2 domain and masks invalid rows (-1 in rows[]) with
-// -inf.  Rows 16mb + 4g + j of the tile are held by this lane; validity comes
-// from one ballot per 64 rows, and fully valid tiles skip the masking.
-template <int kMB>
-__device__ __forceinline__ void scale_and_mask(f32x4 (&sacc)[kMB], const int32_t* rows, float scale,
-                                               int g, int lane) {
-  constexpr int TILE = kMB * 16;
-  uint64_t valid[(TILE + 63) / 64];
-#pragma unroll
-  for (int h = 0; h < (TILE + 63) / 64; ++h)
-    valid[h] = __ballot((h * 64 + lane < TILE) && rows[h * 64 + lane] >= 0);
-  bool all = true;
-#pragma unroll
-  for (int h = 0; h < (TILE + 63) / 64; ++h)
-    all = all && (valid[h] == (TILE - 64 * h >= 64 ? ~0ull : ((1ull << (TILE - 64 * h)) - 1ull)));
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[mb][j] *= scale;
-  if (!all) {
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * mb + 4 * g + j;
-        if (!((valid[r >> 6] >> (r & 63)) & 1ull)) sacc[mb][j] = kNegInf;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 4-wave kernel, tiles of 128 rows.
-constexpr int kThreads4 = 256;
-constexpr int kTile4 = 128;
-
-struct Smem4 {
-  uint16_t k[kTile4 * kKStride];
-  int32_t rows[kRowChunk];
-  int last;                                     // last valid column of the row chunk
-};
-
-// Rows of a 128-row tile prefetched into registers while the previous tile is
-// computed (BF16 rows are twice the bytes: half of them are loaded after).
-template <int KV>
-constexpr int prefetch_rows4() {
-  return KV == DSA_KV_BF16 ? 64 : kTile4;
-}
-
-template <int KV, bool kFinal>
-__global__ __launch_bounds__(kThreads4) void partial4_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) Smem4 sm;
-  constexpr int TILE = kTile4;
-  constexpr int kMB = TILE / 16;
-  constexpr int kKS = TILE / 32;
-  constexpr int kNB = DSA_D_LATENT / 16;
-  constexpr int kPR = prefetch_rows4<KV>();
-
-  const int t = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int c0 = s * a.cols_per_split;
-  const int c1 = min(a.width, c0 + a.cols_per_split);
-  const int req = request_of(a, t);
-  const int pos = a.tok_pos[t];
-
-  u32x4 qf[DSA_D_QK / 32];
-  {
-    const u32x4* qsrc =
-        reinterpret_cast<const u32x4*>(a.q + (int64_t(t) * DSA_HEADS + 16 * wave + c) * DSA_D_QK);
-#pragma unroll
-    for (int ks = 0; ks < DSA_D_QK / 32; ++ks) qf[ks] = qsrc[ks * 4 + g];
-  }
-  __builtin_amdgcn_s_waitcnt(0);   // Q resident before the tile loop
-  f32x4 o[kNB];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf, l_run = 0.f;
-
-  Stage<KV, kPR, kThreads4> st;
-  Stage<KV, (kPR < TILE ? TILE - kPR : 32), kThreads4> st2;  // tail rows (BF16 only)
-  for (int cc = c0; cc < c1; cc += kRowChunk) {
-    const int cend = min(c1, cc + kRowChunk);
-    if (tid == 0) sm.last = -1;
-    __syncthreads();
-    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreads4, &sm.last);
-    __syncthreads();
-    // tiles up to the last valid row (trailing -1 padding is skipped: its rows
-    // would contribute exactly nothing)
-    const int ntile = (sm.last + TILE) / TILE;
-    if (ntile == 0) continue;
-    st.load(a.latent, sm.rows, tid);
-    st.store(sm.k, 0, tid);
-    if constexpr (kPR < TILE) {
-      st2.load(a.latent, sm.rows + kPR, tid);
-      st2.store(sm.k, kPR, tid);
-    }
-    __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-      const bool more = it + 1 < ntile;
-      if (more) st.load(a.latent, sm.rows + (it + 1) * TILE, tid);
-
-      f32x4 sacc[kMB];
-      // logical chunk 4ks + g is physical 4ks + (g ^ bit1(ks))
-      const uint16_t* kq0 = sm.k + c * kKStride + 8 * g;
-      const uint16_t* kq1 = sm.k + c * kKStride + 8 * (g ^ 1);
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DSA_D_QK / 32; ++ks) {
-          const uint16_t* kq = (ks >> 1) & 1 ? kq1 : kq0;
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(kq + 16 * mb * kKStride + 32 * ks);
-          sacc[mb] = dsa::mfma16x16x32(dsa::as_bf16x8(kf), dsa::as_bf16x8(qf[ks]), sacc[mb]);
-        }
-      }
-      scale_and_mask<kMB>(sacc, sm.rows + it * TILE, a.scale_log2, g, lane);
-      u32x4 pa[kKS];
-      softmax_tile<kMB, kNB>(sacc, o, m_ref, l_run, pa, g);
-      pv_tile<kKS, kNB>(sm.k, pa, o, 0, g, c);
-      __syncthreads();
-      if (more) {
-        st.store(sm.k, 0, tid);
-        if constexpr (kPR < TILE) {
-          st2.load(a.latent, sm.rows + (it + 1) * TILE + kPR, tid);
-          st2.store(sm.k, kPR, tid);
-        }
-        __syncthreads();
-      }
-    }
-  }
-
-  const int64_t ts = int64_t(t) * a.splits + s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lj = __shfl(l_run, 4 * g + j);
-    const float inv = lj > 0.f ? 1.f / lj : 0.f;
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) put_out<kFinal>(a, ts, 16 * wave + 4 * g + j, 16 * nb + c, o[nb][j] * inv);
-  }
-  if (g == 0)
-    put_lse<kFinal>(a, ts, 16 * wave + c, l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : kNegInf);
-}
-
 // ---------------------------------------------------------------------------
 // Eight-wave kernel with 32-head waves, tiles of 32 and 64 rows.  Wave w has
 // hp = w&1 (heads 32hp..+32), dh = (w>>1)&1 and rh = w>>2:
@@ -608,7 +391,8 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
   constexpr int kNB = DSA_D_LATENT / 64;     // 16-column blocks per quarter of the 512 (8)
 
   const int t = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hp = wave & 1, dh = (wave >> 1) & 1, rh = wave >> 2;
   const int cq = (wave >> 1) & 3;            // output column quarter (2rh + dh)
   const int g = lane >> 4, c = lane & 15;
@@ -785,27 +569,30 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
     if (!__syncthreads_or(overflow)) break;
   }
 
-  // l of each head = the two row halves' sums; then normalize and write
+  // l of each head = the two row halves' sums; then normalize and write.  The
+  // lane's indices are taken afresh here rather than held through the tile
+  // loop (where they spilled).
+  const int le = dsa::fresh_lane(), ge = le >> 4, ce = le & 15;
   __syncthreads();
-  if (g == 0) sm.red[rh][hp][dh][c] = l_run;
+  if (ge == 0) sm.red[rh][hp][dh][ce] = l_run;
   __syncthreads();
   const int64_t ts = int64_t(t) * a.splits + s;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int hh = 4 * g + j;
+      const int hh = 4 * ge + j;
       const float lj = sm.red[0][hp][hb][hh] + sm.red[1][hp][hb][hh];
       const float inv = lj > 0.f ? 1.f / lj : 0.f;
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
-        put_out<kFinal>(a, ts, 32 * hp + 16 * hb + hh, (DSA_D_LATENT / 4) * cq + 16 * nb + c,
+        put_out<kFinal>(a, ts, 32 * hp + 16 * hb + hh, (DSA_D_LATENT / 4) * cq + 16 * nb + ce,
                         o[hb][nb][j] * inv);
     }
   }
-  if (rh == 0 && g == 0) {
-    const float l = sm.red[0][hp][dh][c] + sm.red[1][hp][dh][c];
-    put_lse<kFinal>(a, ts, 32 * hp + 16 * dh + c, l > 0.f ? (m_ref + log2f(l)) * kLn2 : kNegInf);
+  if (rh == 0 && ge == 0) {
+    const float l = sm.red[0][hp][dh][ce] + sm.red[1][hp][dh][ce];
+    put_lse<kFinal>(a, ts, 32 * hp + 16 * dh + ce, l > 0.f ? (m_ref + log2f(l)) * kLn2 : kNegInf);
   }
 }
 
@@ -832,7 +619,12 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
 // dequantized and stored to LDS once, in small steps placed between the QK
 // MFMAs so that the VALU and LDS work runs beside the matrix pipe.
 constexpr int kTileWS = 32;
-constexpr int kWSValueWaves = 8;            // value waves (4: 128 columns each, 8: 64)
+// Value waves of the warp-specialized kernel: 8 of 64 columns for FP8 rows
+// (12 waves, three per SIMD); 4 of 128 columns for BF16 rows, whose staging
+// (twice the bytes per row) does not fit beside the accumulators in the
+// three-wave register budget.
+template <int KV>
+constexpr int ws_value_waves() { return KV == DSA_KV_FP8_E4M3_S64 ? 8 : 4; }
 constexpr int kWSKLook = 2;                 // k-steps ahead the score waves read K fragments
 constexpr int kPStrideWS = kTileWS;         // bf16 per head in a P buffer (64 bytes)
 
@@ -879,7 +671,7 @@ struct NoStage {
 // a buffer nobody reads.
 template <int KV, int NV, class Stager, class Work>
 __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, int t, int req,
-                                            int pos, int c0, int c1, int tid, int sid,
+                                            int pos, int c0, int c1, int wave, int sid,
                                             Work&& work) {
   constexpr int TILE = kTileWS;
   constexpr int NT = (4 + NV) * 64;
@@ -887,6 +679,7 @@ __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, in
   Stager st[kD];
   for (int cc = c0; cc < c1; cc += kRowChunk) {
     const int cend = min(c1, cc + kRowChunk);
+    const int tid = 64 * wave + dsa::fresh_lane();   // not held through the tile loop
     __syncthreads();                            // every thread has read the last chunk's state
     if (tid == 0) sm.last = -1;
     __syncthreads();
@@ -932,17 +725,20 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
   constexpr int kVCols = DSA_D_LATENT / NV;        // output columns of a value wave
 
   const int t = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = s * a.cols_per_split;
   const int c1 = min(a.width, c0 + a.cols_per_split);
   const int req = request_of(a, t);
   const int pos = a.tok_pos[t];
   const int64_t ts = int64_t(t) * a.splits + s;
 
+  // Each role derives its thread indices itself: the two roles' code is laid
+  // out one after the other, and an index taken before the branch would be
+  // held through the first role's tile loop for the second.
   if (wave < 4) {
     // ---- score wave: heads 16*wave + c (lane column c)
+    const int lane = dsa::fresh_lane(), tid = 64 * wave + lane;
+    const int g = lane >> 4, c = lane & 15;
     const int head = 16 * wave + c;
     u32x4 qf[kQS];   // Q of heads 16*wave..+16, dims 32ks + 8g .. +8 (MFMA B operand)
     {
@@ -955,7 +751,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
     // 4ks + (g ^ bit1(ks))
     const int klane0 = c * kKStride + 8 * g;
     const int klane1 = c * kKStride + 8 * (g ^ 1);
-    ws_pipeline<KV, NV, ScoreStage>(a, sm, t, req, pos, c0, c1, tid, tid, [&](int j, int ntile, auto P) {
+    ws_pipeline<KV, NV, ScoreStage>(a, sm, t, req, pos, c0, c1, wave, tid, [&](int j, int ntile, auto P) {
       constexpr int p = decltype(P)::value;
       if (j < ntile) {
         const uint16_t* kq0 = sm.k[p] + klane0;
@@ -1031,6 +827,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
   } else {
     // ---- value wave: all 64 heads, output columns kVCols*q..+kVCols
     const int q = wave - 4;
+    const int sid = 64 * q + dsa::fresh_lane() + kSidValue0;
     f32x4 o[4][kNB];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
@@ -1039,30 +836,39 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
     // V transpose read: rows 4g + c/4 (+16), columns kVCols*q + 16nb: logical
     // chunk x = (kVCols/8)q + 2nb + (c%4)/2; bit 3 of the even chunk (the same
     // for the whole wave) selects the lane base
-    const int vrow = (4 * g + (c >> 2)) * kKStride + kVCols * q + 4 * (c & 1);
-    const int vlane0 = vrow + 8 * ((c & 3) >> 1);
-    const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
-    ws_pipeline<KV, NV, ValueStage>(a, sm, t, req, pos, c0, c1, tid, tid - 256 + kSidValue0,
+    ws_pipeline<KV, NV, ValueStage>(a, sm, t, req, pos, c0, c1, wave, sid,
                                     [&](int j, int ntile, auto P) {
       constexpr int p = decltype(P)::value;
       if (j >= 1 && j <= ntile) {
         const int jp = j - 1;   // PV of the previous tile, in K buffer (p + 2) % 3
-        // O *= alpha of the heads this lane holds (rows 4g + jj of each head block)
-        f32x4 al[4];
+        // per-lane LDS offsets computed each tile from a fresh lane index (a
+        // few VALU ops) instead of held for all three ring slots through the
+        // loop, where they spilled
+        const int ln = dsa::fresh_lane();
+        const int g = ln >> 4, c = ln & 15;
+        const int vrow = (4 * g + (c >> 2)) * kKStride + kVCols * q + 4 * (c & 1);
+        const int vlane0 = vrow + 8 * ((c & 3) >> 1);
+        const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
+        // O *= alpha of the heads this lane holds (rows 4g + jj of each head
+        // block); the factors are read again in the rare rescale branch rather
+        // than held in registers through it
+        const float* alp = sm.alpha[jp & 1] + 4 * g;
         bool rescale = false;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-          al[hb] = *reinterpret_cast<const f32x4*>(sm.alpha[jp & 1] + 16 * hb + 4 * g);
+          const f32x4 al = *reinterpret_cast<const f32x4*>(alp + 16 * hb);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[hb][jj] != 1.f;
+          for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[jj] != 1.f;
         }
         if (__any(rescale)) {
 #pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
+          for (int hb = 0; hb < 4; ++hb) {
+            const f32x4 al = *reinterpret_cast<const f32x4*>(alp + 16 * hb);
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[hb][jj];
+              for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[jj];
+          }
         }
         const uint16_t* pb = sm.p[jp & 1];
         u32x4 pa[4];
@@ -1092,16 +898,21 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
       }
     });
     __syncthreads();   // the score waves have written each head's sum
+    // the output addresses are derived from a fresh lane index, so the
+    // compiler computes them here instead of keeping them live through the
+    // tile loop (where they spilled)
+    const int lane_e = dsa::fresh_lane();
+    const int ge = lane_e >> 4, ce = lane_e & 15;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int hh = 16 * hb + 4 * g + jj;
+        const int hh = 16 * hb + 4 * ge + jj;
         const float l = sm.fin_l[hh];
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          put_out<kFinal>(a, ts, hh, kVCols * q + 16 * nb + c, o[hb][nb][jj] * inv);
+          put_out<kFinal>(a, ts, hh, kVCols * q + 16 * nb + ce, o[hb][nb][jj] * inv);
       }
   }
 }
@@ -1229,6 +1040,9 @@ struct Q8Stage {
   }
   __device__ __forceinline__ void store(uint8_t* k8, uint8_t* sc8, uint16_t* v, int cid,
                                         int tid) const {
+    // the LDS addresses are computed at each store from opaque copies of the
+    // indices, not hoisted out of the loops and held (they spilled)
+    asm volatile("" : "+v"(cid), "+v"(tid));
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int q = cid + 256 * i, r = q >> 5, c = q & 31;
@@ -1471,13 +1285,17 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
   }
 }
 
+// Tiles of 32 and of 128 index columns run the warp-specialized kernel: a
+// 128-column tile (the plan's loop step and split granularity, Figure 4's
+// virtual padding) is streamed through its three-deep ring as four 32-row LDS
+// steps.  A kernel holding a whole 128-row bf16 tile (148 KB of the 160 KB
+// LDS) had room for neither a second buffer nor more than four waves, spilled
+// 85-98 registers and ran at a third of the tile-32 speed.
 template <int KV, int TILE, bool kFinal>
 hipError_t launch_partial(const PartialArgs& a, int T, int S, hipStream_t st) {
-  if constexpr (TILE == kTile4)
-    hipLaunchKernelGGL((partial4_kernel<KV, kFinal>), dim3(T, S), dim3(kThreads4), 0, st, a);
-  else if constexpr (TILE == kTileWS)
-    hipLaunchKernelGGL((partial_ws_kernel<KV, kFinal, kWSValueWaves>), dim3(T, S),
-                       dim3((4 + kWSValueWaves) * 64), 0, st, a);
+  if constexpr (TILE == kTileWS || TILE == 128)
+    hipLaunchKernelGGL((partial_ws_kernel<KV, kFinal, ws_value_waves<KV>()>), dim3(T, S),
+                       dim3((4 + ws_value_waves<KV>()) * 64), 0, st, a);
   else
     hipLaunchKernelGGL((partial_v2_kernel<KV, TILE, kFinal>), dim3(T, S), dim3(kThreadsV2), 0, st, a);
   return hipGetLastError();

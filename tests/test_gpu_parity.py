@@ -55,9 +55,10 @@ def test_full_path_tiles_and_splits(tile, splits):
 
 @pytest.mark.parametrize("tile,splits", [(128, 1), (128, 2), (64, 2)])
 def test_bf16_partial_splits_against_oracle(tile, splits):
-    # BF16 rows at tile 128 (the kernel stages part of each 128-row tile
-    # separately for the wider rows), with one and with several splits: every
-    # split's (o, lse) and the combined output against the oracle
+    # BF16 rows at tile 128 (the warp-specialized kernel's BF16 form, 4 value
+    # waves; splits cut at multiples of 128 columns) and at tile 64, with one
+    # and with several splits: every split's (o, lse) and the combined output
+    # against the oracle
     wl = _gen("tiny_bf16", seed=12)
     hv = HostView(wl)
     pool = make_pool(wl)
@@ -136,10 +137,11 @@ def test_partial_later_tile_far_above_first_tile():
     # One row of request 1 gets a score about 200 (natural units, sm_scale 1)
     # above everything before it in the index, and it sits at index column
     # 152: in the fifth tile at tile 32, the third at tile 64 and the second
-    # at tile 128.  The tile-32/64 kernel's reference max, fixed by the first
+    # at tile 128.  At tile 64 the kernel's reference max, fixed by the first
     # tile, is then far too low and the split is recomputed with the exact max;
-    # the tile-128 kernel's running max grows by more than its rescale
-    # threshold and O is rescaled.  Every form must match the oracle.
+    # at tiles 32 and 128 the warp-specialized kernel's running max grows by
+    # more than its rescale threshold and O is rescaled.  Every form must
+    # match the oracle.
     wl = synth.generate(synth.spec("tiny_bf16"), seed=7, device="cpu")
     b, t, p_hi = 1, 3, 120
     assert int(wl.tok_req[t]) == b and int(wl.tok_pos[t]) >= 300
