@@ -49,6 +49,10 @@ constexpr int kCoarseBits = 12;                // top key bits of the first hist
 constexpr int kBins = 1 << kCoarseBits;        // 4096
 constexpr int kFineBits = 10;                  // 32 - 12 = 20 remaining bits = 2 x 10
 constexpr int kCap = 4096;                     // threshold-bin candidates kept in LDS
+// Score bits of an empty slot in a segment's candidate list: a NaN (scores
+// never are), whose order key is 0, the key of "no element"; the merge tells
+// empty slots by the score alone, without loading their positions.
+constexpr uint32_t kEmptyBits = 0xFFFFFFFFu;
 
 static_assert(kSeg == dsa::kTopkSeg, "segment size must match the host side");
 
@@ -145,8 +149,9 @@ struct IndexIn {
 // at 1024*i + 64*v; its four 16-position MFMA blocks use the same operand
 // layouts, accumulation order and epilogue as the indexer, so the bits match.
 // Positions at or past n are left 0 (masked by the caller).
-__device__ __forceinline__ void fallback_scores(uint32_t (&key)[kEPT], const IndexIn& f, int t, int n) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void fallback_scores(uint32_t (&key)[kEPT], const IndexIn& f, int t, int n,
+                                                int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   int lo = 0, hi = f.num_reqs;   // request b with q_offsets[b] <= t < q_offsets[b+1]
   while (hi - lo > 1) {
@@ -206,7 +211,11 @@ __device__ __forceinline__ void topk_row(Smem& sm, const RowArgs& a, int t, int 
   float* __restrict__ cand_val = a.cand_val;
   int32_t* __restrict__ cand_pos = a.cand_pos;
   int32_t* __restrict__ idx_out = a.idx_out;
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // the fallback runs one row after another in a loop: an opaque copy of the
+  // thread index keeps its per-thread addresses inside the row instead of
+  // hoisted out of the loop and held (they spilled)
+  if constexpr (MODE == kFallback) asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
 
   // ---- row geometry
@@ -237,7 +246,7 @@ __device__ __forceinline__ void topk_row(Smem& sm, const RowArgs& a, int t, int 
   const int cnt = n > tid ? (n - tid + kThreads - 1) / kThreads : 0;
   const int last = max(n - 1, 0);
   if constexpr (MODE == kFallback) {
-    fallback_scores(key, f, t, n);
+    fallback_scores(key, f, t, n, tid);
   } else {
 #pragma unroll
     for (int i = 0; i < kEPT; ++i) {
@@ -249,7 +258,7 @@ __device__ __forceinline__ void topk_row(Smem& sm, const RowArgs& a, int t, int 
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
     bool ok = i < cnt;
-    if (MODE == kMerge) ok = ok && vpos[min(kThreads * i + tid, last)] >= 0;
+    if (MODE == kMerge) ok = ok && key[i] != kEmptyBits;   // an empty segment slot
     key[i] = ok ? dsa::float_key(__uint_as_float(key[i])) : 0u;
     my_valid += ok ? 1u : 0u;
     if (ok) atomicAdd(&sm.hist[key[i] >> (32 - kCoarseBits)], 1u);
@@ -411,7 +420,7 @@ __device__ __forceinline__ void topk_row(Smem& sm, const RowArgs& a, int t, int 
   for (int i = int(total) + tid; i < limit; i += kThreads) {
     if (MODE == kSegment) {
       const int64_t o = (int64_t(t) * nseg + seg) * kc + i;
-      cand_val[o] = 0.f;
+      cand_val[o] = __uint_as_float(kEmptyBits);
       cand_pos[o] = -1;
     } else {
       idx_out[int64_t(t) * k + i] = -1;

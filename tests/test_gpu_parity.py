@@ -373,6 +373,10 @@ def test_topk_long_rows_two_stage():
     T, L, k = 3, 200_000, 700
     g = torch.Generator().manual_seed(12)
     sc = torch.randint(0, 1000, (T, L), generator=g).float()
+    # token 1 sees one position of its third segment and token 2 none past
+    # the first, so their segment lists hold empty slots; token 1's scores
+    # are negative, so an empty slot read as a score would outrank them
+    sc[1] = -1.0 - sc[1]
     tok_pos = torch.tensor([L - 1, 131_072, 65_535], dtype=torch.int32)
     say("[case] topk long rows")
     idx = dsa.topk(sc.to(DEV), tok_pos.to(DEV), k, L).cpu().numpy()
