@@ -545,11 +545,14 @@ def bench_q8(dsa, spec, wl, pool, path, stream, flush, steps, flops_partial):
             "note": "same selected rows as the bf16 Partial above; FLOPs counted as for it"}
 
 
-def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=10, warmup=3, tiles=(32, 64, 128)):
+def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=7, warmup=10, rounds=5,
+                        tiles=(32, 64, 128)):
     """132 requests sharing a 63,488-token prefix: Partial at KV tiles 32, 64
-    and 128 (one split each) on the same selected indices.  Logical bytes are
-    the rows as gathered; unique bytes count each physical row once (the
-    shared rows come from the caches, so HBM sees about the unique bytes)."""
+    and 128 (one split each) on the same selected indices, timed in
+    interleaved rounds (each tile's figure is the median of its round
+    medians).  Logical bytes are the rows as gathered; unique bytes count each
+    physical row once (the shared rows come from the caches, so HBM sees
+    about the unique bytes)."""
     import statistics
     spec, wl, pool, path, _, _ = setup_path(dsa, synth, "shared_prefix_fp8", dev, cus)
     stream = torch.cuda.current_stream(dev)
@@ -564,7 +567,7 @@ def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=10, warmup=3, tiles=(
     fixed = T * k * 4 + T * 64 * 576 * 2 + T * 64 * (512 * 2 + 4)     # idx, q, output
     logical = fixed + T * k * lay.latent_row_bytes
     unique = fixed + uniq_rows * lay.latent_row_bytes
-    res = {}
+    calls = {}
     for tile in tiles:
         out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
@@ -572,17 +575,30 @@ def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=10, warmup=3, tiles=(
         def call(tile=tile, out=out, lse=lse):
             dsa.sparse_mla(pool, wl.page_table, wl.q_offsets, wl.tok_pos, wl.q, path.idx,
                            spec.sm_scale, tile, out, lse)
+        calls[tile] = call
         for _ in range(warmup):
             call()
-        step_ms, _ = time_steps([call], ["partial"], steps, stream, flush)
-        us = 1000.0 * statistics.median(step_ms)
+    # the tiles take turns, round after round, so that drift over the run
+    # (a fresh process runs its first kernels slower) reaches every tile alike
+    per_round = {tile: [] for tile in tiles}
+    for _ in range(rounds):
+        for tile in tiles:
+            step_ms, _ = time_steps([calls[tile]], ["partial"], steps, stream, flush)
+            per_round[tile].append(statistics.median(step_ms))
+    res = {}
+    for tile in tiles:
+        us = 1000.0 * statistics.median(per_round[tile])
         res[str(tile)] = {"avg_us": round(us, 1),
                           "logical_gbps": round(logical / (us * 1e-6) / 1e9, 1),
-                          "unique_gbps": round(unique / (us * 1e-6) / 1e9, 1)}
+                          "unique_gbps": round(unique / (us * 1e-6) / 1e9, 1),
+                          "rounds_us": [round(1000.0 * x, 1) for x in per_round[tile]]}
     out = {"workload": spec.name, "query_tokens": T, "splits": 1, "partial_by_tile": res,
            "logical_bytes": int(logical), "unique_bytes": int(unique), "unique_rows": uniq_rows,
            "tile128_speedup_over_tile32": round(res["32"]["avg_us"] / res["128"]["avg_us"], 3),
-           "note": "one split per token; the pages report Partial + Combine at KV tile 128 about "
+           "timing": f"{rounds} interleaved rounds of {steps} cache-flushed steps per tile; median "
+                     f"of the round medians",
+           "note": "one split per token; tiles 32 and 128 run the same kernel (a 128-column tile "
+                   "streams through LDS as four 32-row steps); the pages report Partial + Combine at KV tile 128 about "
                    "1.12x faster than at tile 32 on H200 (context, other hardware)"}
     pool.close()
     del wl, path, pool
