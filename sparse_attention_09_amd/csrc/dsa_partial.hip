@@ -644,12 +644,12 @@ struct SmemWS {
   int last;
 };
 
-// Tiles gathered ahead into registers: 3 for FP8 rows in the 8-wave form; 1
-// for BF16 rows (twice the bytes) and in the 12-wave form, whose 168-register
-// budget holds one staged tile beside the accumulators (three spilled inside
-// the tile loop and ran 15% slower).
+// Tiles gathered ahead into registers (the pipeline takes 1 or 3): one.  The
+// 12-wave FP8 form's 168-register budget holds one staged tile beside the
+// value waves' accumulators (a three-tile lead spills 26 VGPRs; an earlier
+// spilling build of it ran 15% slower), and BF16 rows are twice the bytes.
 template <int KV, int NV>
-constexpr int ws_depth() { return KV == DSA_KV_FP8_E4M3_S64 && NV == 4 ? 3 : 1; }
+constexpr int ws_depth() { return 1; }
 
 // Waves that stage nothing (the score waves of the 12-wave form).
 struct NoStage {
