@@ -400,9 +400,10 @@ def time_steps(calls, names, steps, stream, flush=None):
     return step_ms, per_us
 
 
-def measure_peaks(dev, reps=10):
-    """The box's own denominators: a 1 GiB device copy (GB/s, read + write)
-    and an 8192^3 bf16 GEMM through torch (TFLOP/s, dense MFMA)."""
+def measure_peaks(dsa, dev, reps=10):
+    """The box's own denominators: a 1 GiB device copy (GB/s, read + write),
+    a 2 GiB read (the library's read probe: the bound of a kernel that mostly
+    reads) and an 8192^3 bf16 GEMM through torch (TFLOP/s, dense MFMA)."""
     a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -415,6 +416,17 @@ def measure_peaks(dev, reps=10):
     torch.cuda.synchronize()
     copy_gbps = 2 * 4 * a.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
+    r = torch.ones(1 << 29, dtype=torch.int32, device=dev)
+    words = torch.empty(2048, dtype=torch.int32, device=dev)
+    dsa.read_probe(r, words)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dsa.read_probe(r, words)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbps = 4 * r.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del r, words
     n = 8192
     g = torch.Generator(device=dev).manual_seed(1)
     x = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
@@ -429,8 +441,10 @@ def measure_peaks(dev, reps=10):
     gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del x, y, z
     torch.cuda.empty_cache()
-    return {"copy_gbps": round(copy_gbps, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+    return {"copy_gbps": round(copy_gbps, 1), "read_gbps": round(read_gbps, 1),
+            "bf16_gemm_tflops": round(gemm_tflops, 1),
             "copy": "1 GiB device-to-device copy (bytes read + written)",
+            "read": "2 GiB read once by dsa_read_probe (2048 workgroups, 16-byte loads)",
             "gemm": "8192 x 8192 x 8192 bf16 torch.matmul"}
 
 
@@ -730,7 +744,7 @@ def main():
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
     T = spec.num_tokens
     value = T / (ms_step * 1e-3)
-    peaks = None if args.no_extra else measure_peaks(dev)
+    peaks = None if args.no_extra else measure_peaks(dsa, dev)
     # the decode batches are bound by HBM: the roof of the dominant kernel is
     # its algorithmic bytes over the HBM peak (also given against the box's
     # measured copy bandwidth)
@@ -739,8 +753,11 @@ def main():
             "traffic": measured_traffic(spec.name, dom),
             "alg_bytes_per_launch": int(byts[dom]), "avg_us": kernels[dom]["avg_us"]}
     if peaks:
-        roof["measured_peak"] = peaks["copy_gbps"]
-        roof["frac_of_measured"] = round(kernels[dom]["gbps"] / peaks["copy_gbps"], 4)
+        # the selection and the attention mostly read: the box's read rate is
+        # their measured ceiling (its copy rate is lower and also reported)
+        roof["measured_peak"] = peaks["read_gbps"]
+        roof["frac_of_measured"] = round(kernels[dom]["gbps"] / peaks["read_gbps"], 4)
+        roof["frac_of_measured_copy"] = round(kernels[dom]["gbps"] / peaks["copy_gbps"], 4)
     for n in names:
         kernels[n]["traffic_bytes"] = measured_traffic(spec.name, n)
         if n in ("partial", "index_topk"):

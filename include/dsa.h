@@ -377,6 +377,17 @@ dsa_status dsa_kv_append(const dsa_pool* pool, const int32_t* page_table, int32_
                          int32_t num_reqs, const int32_t* req, const int32_t* pos, int32_t n,
                          const uint16_t* latent, const uint16_t* keys, void* stream);
 
+/* Measurement utility, not a step of the path: the denominator that the
+ * HBM-bound kernels' rooflines are compared against beside the vendor peak.
+ * Reads `bytes` of device memory at `buf` once, in 16-byte loads spread over
+ * `num_blocks` workgroups of 256 threads (a grid-stride loop), and writes one
+ * uint32 per workgroup (the XOR of the words it read) to out[0..num_blocks).
+ * buf and out: device, buf 16-byte aligned, bytes a multiple of 16 (0: no
+ * launch); num_blocks in [1, 65536].  DSA_ERR_INVALID_ARG otherwise.
+ * Asynchronous on `stream`. */
+dsa_status dsa_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_blocks,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

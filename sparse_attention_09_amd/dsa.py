@@ -40,7 +40,7 @@ EXPORTS = [
     "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk", "dsa_plan_partial",
     "dsa_sparse_mla_partial", "dsa_sparse_mla", "dsa_combine", "dsa_kv_append",
     "dsa_index_topk_workspace_bytes", "dsa_index_topk", "dsa_dcp_merge", "dsa_combine_shards",
-    "dsa_topk_noalloc", "dsa_quantize_q8", "dsa_sparse_mla_q8",
+    "dsa_topk_noalloc", "dsa_quantize_q8", "dsa_sparse_mla_q8", "dsa_read_probe",
 ]
 
 
@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
             "dsa_combine_shards": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "dsa_index_topk": (i32, [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, i32, i32, i32,
                                      vp, vp, sz, vp]),
+            "dsa_read_probe": (i32, [vp, i64, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -369,6 +370,18 @@ def sparse_mla(pool: Pool, page_table, q_offsets, tok_pos, q, idx, sm_scale: flo
                                 idx.shape[-1], float(sm_scale), kv_tile, _ptr(out), _ptr(lse),
                                 _stream(dev)))
     return out, lse
+
+
+def read_probe(buf: torch.Tensor, out: torch.Tensor):
+    """Reads all of `buf` once (a measurement of the read bandwidth, not a
+    step of the path); out: int32 [num_blocks], one word per workgroup."""
+    if not buf.is_contiguous() or not out.is_contiguous() or out.dtype != torch.int32:
+        raise ValueError("read_probe: contiguous buf and a contiguous int32 out")
+    if buf.device != out.device:
+        raise ValueError("read_probe: buf and out on one device")
+    _check(lib().dsa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                out.numel(), _stream(buf.device)))
+    return out
 
 
 def quantize_q8(q: torch.Tensor, codes=None, scales=None):

@@ -300,6 +300,15 @@ def test_compute_calls_validate_before_launch():
     assert L.dsa_kv_append(h, f, 4, 1, f, f, 1, vp(FAKE + 8), None, None) == 1
     assert L.dsa_kv_append(h, f, 4, 1, f, f, 1, f, vp(FAKE + 4), None) == 1
     assert L.dsa_kv_append(h, None, 4, 1, None, None, 0, None, None, None) == 0
+    # read probe: pointers, size, alignment, grid bounds; 0 bytes launches nothing
+    assert L.dsa_read_probe(None, 64, f, 1, None) == 1
+    assert L.dsa_read_probe(f, 64, None, 1, None) == 1
+    assert L.dsa_read_probe(f, 60, f, 1, None) == 1
+    assert L.dsa_read_probe(f, -16, f, 1, None) == 1
+    assert L.dsa_read_probe(vp(FAKE + 4), 64, f, 1, None) == 1
+    assert L.dsa_read_probe(f, 64, f, 0, None) == 1
+    assert L.dsa_read_probe(f, 64, f, 65537, None) == 1
+    assert L.dsa_read_probe(f, 0, f, 1, None) == 0
     # empty batches are valid no-ops
     assert L.dsa_combine(None, None, 0, 1, None, None, None) == 0
     assert L.dsa_topk(None, 64, None, 0, 64, 8, None, None, 0, None) == 0
