@@ -698,19 +698,28 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
   }
   const int N = int(n);
   // compaction, all loads of a thread in flight together: candidate q is slot
-  // q - off[j] of the chunk j holding it
+  // q - off[j] of the chunk j holding it.  The chunk of every candidate is
+  // first written into pos[] (its slots, by the chunk's thread), so each
+  // candidate takes two independent LDS reads (a binary search over the
+  // offsets is seven dependent ones per candidate, and they ran one after
+  // another).
+  if (tid < nch_t)
+    for (int s2 = 0; s2 < c; ++s2) sm.pos[o + s2] = uint16_t(tid);
+  __syncthreads();
   constexpr int kPer = kSelMax / kSmallThreads;
+  int chunk_of[kPer], first_of[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = sm.pos[kSmallThreads * u + tid];   // stale past N: clamped below
+    chunk_of[u] = j < nch_t ? j : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) first_of[u] = sm.off[chunk_of[u]];
   int64_t src[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int q = kSmallThreads * u + tid;
-    int j = 0;
-#pragma unroll
-    for (int step = kMaxChunks / 2; step > 0; step >>= 1) {
-      const int m = j + step;
-      if (m < nch_t && sm.off[m] <= q) j = m;
-    }
-    src[u] = q < N ? (int64_t(t) * nch + j) * capr + 1 + (q - sm.off[j]) : -1;
+    src[u] = q < N ? (int64_t(t) * nch + chunk_of[u]) * capr + 1 + (q - first_of[u]) : -1;
   }
   // loads unconditional (an unused slot reads the token's first slot) so all
   // are in flight at once; LDS writes after
