@@ -732,16 +732,20 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
     v[u] = __int_as_float(x.x);
     pv[u] = x.y;
   }
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  // the keys stay in registers for the radix passes (read back from LDS they
+  // were one dependent read per key and pass)
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, held = 0u;
+  uint32_t kreg[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
+    kreg[u] = dsa::float_key(v[u]);
     if (src[u] >= 0) {
-      const uint32_t key = dsa::float_key(v[u]);
       const int q = kSmallThreads * u + tid;
-      sm.key[q] = key;
+      sm.key[q] = kreg[u];
       sm.pos[q] = uint16_t(pv[u]);
-      lo = min(lo, key);
-      hi = max(hi, key);
+      lo = min(lo, kreg[u]);
+      hi = max(hi, kreg[u]);
+      held |= 1u << u;
     }
   }
   uint32_t kmin, kmax, unused;
@@ -750,7 +754,9 @@ __global__ __launch_bounds__(kSmallThreads) void select_kernel(
   const uint32_t tau = radix_select256(
       sm.s, uint32_t(k), kmin, kmax,
       [&](auto&& f) {
-        for (int q = tid; q < N; q += kSmallThreads) f(sm.key[q]);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          if ((held >> u) & 1u) f(kreg[u]);
       },
       &r);
   // thread i owns candidates [E*i, E*i + E): equal keys kept lowest position first
