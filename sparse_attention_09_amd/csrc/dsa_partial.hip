@@ -313,29 +313,62 @@ struct Stage<DSA_KV_BF16, NR, NT> {
 // 0 for a valid row and -inf for a masked one.  *last (reset to -1 by the
 // caller) receives the largest chunk-relative column with a valid row.
 // nthreads must divide N (the column count, kRowChunk by default).
-template <int N = kRowChunk>
+// Physical rows of index columns [cc, cend) of token t (-1 where the entry is
+// masked), written to rows[0..N) (and bias: 0 or -inf); *last gets the largest
+// slot holding a valid row.  NT threads; each thread takes its columns in
+// batches of kB, the batch's index loads in flight together, then its
+// page-table loads (the plain loop, kB = 0, waits for each column's two loads
+// in turn: six memory latencies at 2,048 columns over 768 threads).
+template <int N, int NT, int kB = (N + NT - 1) / NT>
 __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int req, int pos, int cc,
-                                             int cend, int32_t* rows, int tid, int nthreads,
-                                             int* last, float* bias = nullptr) {
+                                             int cend, int32_t* rows, int tid, int* last,
+                                             float* bias = nullptr) {
+  static_assert(N % 64 == 0 && NT % 64 == 0, "whole waves per pass");
+  constexpr int kIt = (N + NT - 1) / NT;
   const int lane = tid & 63;
-  for (int i = tid; i < N; i += nthreads) {
-    const int col = cc + i;
-    int phys = -1;
-    if (col < cend) {
-      const int p = a.idx[int64_t(t) * a.width + col];
-      if (p >= 0 && p <= pos) {
-        const int j = p >> 6;
-        if (j < a.pt_stride) {
-          int pg = a.page_table[int64_t(req) * a.pt_stride + j];
-          pg = min(max(pg, 0), a.num_pages - 1);
-          phys = pg * DSA_PAGE_TOKENS + (p & 63);
+  if constexpr (kB == 0) {
+    for (int i = tid; i < N; i += NT) {
+      const int col = cc + i;
+      int phys = -1;
+      if (col < cend) {
+        const int p = a.idx[int64_t(t) * a.width + col];
+        if (p >= 0 && p <= pos && (p >> 6) < a.pt_stride) {
+          const int pg = a.page_table[int64_t(req) * a.pt_stride + (p >> 6)];
+          phys = min(max(pg, 0), a.num_pages - 1) * DSA_PAGE_TOKENS + (p & 63);
         }
       }
+      rows[i] = phys;
+      if (bias) bias[i] = phys >= 0 ? 0.f : kNegInf;
+      const uint64_t m = __ballot(phys >= 0);
+      if (m != 0ull && lane == 0) atomicMax(last, i + 63 - __clzll((long long)m));
     }
-    rows[i] = phys;
-    if (bias) bias[i] = phys >= 0 ? 0.f : kNegInf;
-    const uint64_t m = __ballot(phys >= 0);
-    if (m != 0ull && lane == 0) atomicMax(last, i + 63 - __clzll((long long)m));
+    return;
+  }
+#pragma unroll
+  for (int u0 = 0; u0 < kIt; u0 += (kB > 0 ? kB : 1)) {
+    int p[kB > 0 ? kB : 1], pg[kB > 0 ? kB : 1];
+#pragma unroll
+    for (int v = 0; v < kB; ++v) {
+      const int i = tid + NT * (u0 + v), col = cc + i;
+      p[v] = (u0 + v < kIt && i < N && col < cend) ? a.idx[int64_t(t) * a.width + col] : -1;
+    }
+#pragma unroll
+    for (int v = 0; v < kB; ++v) {
+      const bool ok = p[v] >= 0 && p[v] <= pos && (p[v] >> 6) < a.pt_stride;
+      pg[v] = ok ? a.page_table[int64_t(req) * a.pt_stride + (p[v] >> 6)] : -1;
+      if (ok) pg[v] = min(max(pg[v], 0), a.num_pages - 1);
+    }
+#pragma unroll
+    for (int v = 0; v < kB; ++v) {
+      const int i = tid + NT * (u0 + v);
+      if (u0 + v < kIt && i < N) {   // wave-uniform
+        const int phys = pg[v] >= 0 ? pg[v] * DSA_PAGE_TOKENS + (p[v] & 63) : -1;
+        rows[i] = phys;
+        if (bias) bias[i] = phys >= 0 ? 0.f : kNegInf;
+        const uint64_t m = __ballot(phys >= 0);
+        if (m != 0ull && lane == 0) atomicMax(last, i + 63 - __clzll((long long)m));
+      }
+    }
   }
 }
 
@@ -546,7 +579,9 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
       const int cend = min(c1, cc + kRowChunk);
       if (tid == 0) sm.last = -1;
       __syncthreads();
-      resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
+      // the plain loop: with the accumulators live here, the batched form
+      // spilled 3-4 VGPRs in this 256-register kernel
+      resolve_rows<kRowChunk, kThreadsV2, 0>(a, t, req, pos, cc, cend, sm.rows, tid, &sm.last, sm.bias);
       __syncthreads();
       // tiles up to the last valid row (trailing -1 padding is skipped: its
       // rows would contribute exactly nothing)
@@ -683,7 +718,7 @@ __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, in
     __syncthreads();                            // every thread has read the last chunk's state
     if (tid == 0) sm.last = -1;
     __syncthreads();
-    resolve_rows(a, t, req, pos, cc, cend, sm.rows, tid, NT, &sm.last, sm.bias);
+    resolve_rows<kRowChunk, NT>(a, t, req, pos, cc, cend, sm.rows, tid, &sm.last, sm.bias);
     __syncthreads();
     const int ntile = (sm.last + TILE) / TILE;
     if (ntile == 0) continue;
@@ -1088,7 +1123,7 @@ __device__ __forceinline__ void q8_pipeline(const PartialArgs& a, SmemQ8& sm, in
     __syncthreads();
     if (tid == 0) sm.last = -1;
     __syncthreads();
-    resolve_rows<kRowChunkQ8>(a, t, req, pos, cc, cend, sm.rows, tid, kThreadsV2, &sm.last, sm.bias);
+    resolve_rows<kRowChunkQ8, kThreadsV2>(a, t, req, pos, cc, cend, sm.rows, tid, &sm.last, sm.bias);
     __syncthreads();
     const int ntile = (sm.last + kTileQ8) / kTileQ8;
     if (ntile == 0) continue;
