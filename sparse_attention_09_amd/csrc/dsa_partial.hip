@@ -372,13 +372,37 @@ __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int re
   }
 }
 
+// Request of token t: q_offsets is nondecreasing with q_offsets[0] = 0, so the
+// request is (the number of requests r with q_offsets[r] <= t) - 1, counted
+// by every wave with ballots over one vector load per lane and request block
+// (a binary search was one dependent load per halving, ~7 latencies at 128
+// requests, before anything else could start).  Whole waves, uniform flow.
 __device__ __forceinline__ int request_of(const PartialArgs& a, int t) {
-  int lo = 0, hi = a.num_reqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.q_offsets[mid] <= t) lo = mid; else hi = mid - 1;
+  constexpr int kFirst = 4;   // 256 requests in the first round trip
+  const int lane = dsa::fresh_lane();
+  int below = 0;
+  bool more = true;
+  int le[kFirst];
+#pragma unroll
+  for (int i = 0; i < kFirst; ++i) {
+    const int r = 64 * i + lane;
+    le[i] = r < a.num_reqs ? a.q_offsets[r] : 0x7fffffff;
   }
-  return lo;
+#pragma unroll
+  for (int i = 0; i < kFirst; ++i) {
+    const uint64_t m = __ballot(le[i] <= t);
+    if (more) below += __popcll(m);
+    more = more && m == ~0ull;
+  }
+  for (int base = 64 * kFirst; more && base < a.num_reqs; base += 64) {
+    const int r = base + lane;
+    const uint64_t m = __ballot(r < a.num_reqs && a.q_offsets[r] <= t);
+    below += __popcll(m);
+    more = m == ~0ull;
+  }
+  // clamped into [0, num_reqs) like any request index (malformed offsets
+  // then read a wrong request's pages, never out of the page table)
+  return min(max(below - 1, 0), a.num_reqs - 1);
 }
 
 // ---------------------------------------------------------------------------
