@@ -344,19 +344,32 @@ __device__ __forceinline__ void resolve_rows(const PartialArgs& a, int t, int re
     }
     return;
   }
+  // loads unconditional (a column past the range reads the range's last one
+  // or column 0, a masked entry page 0 of the request) and masked afterwards:
+  // a conditional load compiles to a branch that waits for it, one load at a
+  // time
+  const int32_t* idx_row = a.idx + int64_t(t) * a.width;
+  const int32_t* pt = a.page_table + int64_t(req) * a.pt_stride;
+  const int col_max = max(cend - 1, 0);
 #pragma unroll
   for (int u0 = 0; u0 < kIt; u0 += (kB > 0 ? kB : 1)) {
     int p[kB > 0 ? kB : 1], pg[kB > 0 ? kB : 1];
 #pragma unroll
+    for (int v = 0; v < kB; ++v) p[v] = idx_row[min(cc + tid + NT * (u0 + v), col_max)];
+#pragma unroll
     for (int v = 0; v < kB; ++v) {
-      const int i = tid + NT * (u0 + v), col = cc + i;
-      p[v] = (u0 + v < kIt && i < N && col < cend) ? a.idx[int64_t(t) * a.width + col] : -1;
+      const int i = tid + NT * (u0 + v);
+      if (!(u0 + v < kIt && i < N && cc + i < cend)) p[v] = -1;
     }
 #pragma unroll
     for (int v = 0; v < kB; ++v) {
       const bool ok = p[v] >= 0 && p[v] <= pos && (p[v] >> 6) < a.pt_stride;
-      pg[v] = ok ? a.page_table[int64_t(req) * a.pt_stride + (p[v] >> 6)] : -1;
-      if (ok) pg[v] = min(max(pg[v], 0), a.num_pages - 1);
+      pg[v] = pt[ok ? (p[v] >> 6) : 0];
+    }
+#pragma unroll
+    for (int v = 0; v < kB; ++v) {
+      const bool ok = p[v] >= 0 && p[v] <= pos && (p[v] >> 6) < a.pt_stride;
+      pg[v] = ok ? min(max(pg[v], 0), a.num_pages - 1) : -1;
     }
 #pragma unroll
     for (int v = 0; v < kB; ++v) {
