@@ -47,6 +47,29 @@ def test_full_path_small(name):
     _check_full_path(_gen(name))
 
 
+def test_many_requests_some_empty():
+    # 300 requests, a fifth of them with no query token (equal consecutive
+    # offsets): the kernels find a token's request by counting the offsets
+    # at or below it, 256 requests in the first round and 64 at a time after,
+    # so tokens of requests past 256 and next to empty ones are checked
+    g = np.random.default_rng(31)
+    R = 300
+    ctx = [int(x) for x in g.integers(40, 260, size=R)]
+    q = [int(x) for x in g.integers(0, 3, size=R)]
+    for b in (0, 255, 256, 257, R - 1):
+        q[b] = max(q[b], 1)
+    for b in (254, 258, 290):
+        q[b] = 0
+    spec = synth.Spec("many_reqs_fp8", synth.KV_FP8, ctx, q, 32)
+    wl = synth.generate(spec, seed=5, device="cpu").to(DEV)
+    assert spec.num_reqs == R and sum(1 for x in q if x == 0) > 0
+    offs = np.cumsum([0] + q)
+    late = [t for t in range(int(offs[255]), spec.num_tokens)]
+    early = list(range(0, 12))
+    for tile, splits in ((32, 1), (64, 1)):
+        _check_full_path(wl, tile, splits, tokens=early + late)
+
+
 @pytest.mark.parametrize("tile,splits", [(32, 1), (32, 3), (64, 1), (64, 2), (32, 40), (128, 1),
                                          (128, 3)])
 def test_full_path_tiles_and_splits(tile, splits):
