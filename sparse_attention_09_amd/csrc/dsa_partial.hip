@@ -22,7 +22,8 @@
 //     the gfx950 transpose read (ds_read_b64_tr_b16), so no transposed copy is
 //     made.
 // Kernels:
-//   * tiles of 32 and 128 index columns (partial_ws_kernel): 12 waves in a
+//   * tiles of 32 and 128 index columns (partial_ws_kernel): 12 waves (8 for
+//     BF16 rows) in a
 //     score role and a value role one 32-row tile apart, a running reference
 //     max that rescales O only when it grows by more than 2^8 (described at
 //     the kernel); a 128-column tile is four of its 32-row LDS steps;
@@ -669,27 +670,27 @@ __global__ __launch_bounds__(kThreadsV2) void partial_v2_kernel(PartialArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialized kernel, tiles of 32 rows: 8 waves, one workgroup per
-// (token, split), two roles with one wave of each on every SIMD.
+// Warp-specialized kernel, tiles of 32 rows: one workgroup per (token,
+// split), two roles, every SIMD running one score wave beside its value waves.
 //   * Score waves 0..3: wave w computes S^T for heads 16w..+16 over all 576
 //     dims and the tile's 32 rows (the Q of its heads stays in registers, so
 //     no partial sums are exchanged between waves), runs the online softmax
 //     with a running per-head max (O is rescaled only when a head's max grows
 //     by more than 2^8) and writes P and the per-head rescale factor to LDS.
-//   * Value waves 4..7: wave 4+q accumulates O for all 64 heads on output
-//     columns 128q..+128; each transposed V fragment read feeds four head
-//     blocks.
+//   * Value waves: O for all 64 heads on a slice of the output columns, 8
+//     waves of 64 columns for FP8 rows (12 waves, three per SIMD) or 4 of 128
+//     for BF16 rows (8 waves); each transposed V fragment read feeds four
+//     head blocks.
 // The roles run one tile apart: in iteration j the score waves work on tile
 // j while the value waves run PV of tile j-1, so on each SIMD one wave's
-// MFMAs can overlap the other wave's softmax and staging work instead of
+// MFMAs can overlap the other waves' softmax and staging work instead of
 // every wave passing through the same phase between barriers.  K tiles are a
 // ring of three bf16 buffers (score waves read tile j, value waves tile j-1,
 // tile j+1 is staged into the third) and P a ring of two: one barrier per
-// tile.  The score waves also stage (the value waves hold the 128-register O
-// accumulator and have no room): the selected rows are gathered kD tiles ahead
-// into their registers (3 for FP8 rows, 1 for the wider BF16 rows),
-// dequantized and stored to LDS once, in small steps placed between the QK
-// MFMAs so that the VALU and LDS work runs beside the matrix pipe.
+// tile.  The selected rows are gathered two tiles ahead into registers and
+// dequantized and stored to LDS after the role work: by the value waves for
+// FP8 rows (the score waves' registers hold their Q), by every thread for
+// the wider BF16 rows.
 constexpr int kTileWS = 32;
 // Value waves of the warp-specialized kernel: 8 of 64 columns for FP8 rows
 // (12 waves, three per SIMD); 4 of 128 columns for BF16 rows, whose staging
@@ -716,12 +717,11 @@ struct SmemWS {
   int last;
 };
 
-// Tiles gathered ahead into registers (the pipeline takes 1 or 3): one.  The
-// 12-wave FP8 form's 168-register budget holds one staged tile beside the
-// value waves' accumulators (a three-tile lead spills 26 VGPRs; an earlier
-// spilling build of it ran 15% slower), and BF16 rows are twice the bytes.
+// Tiles gathered ahead into registers: two.  A load then has two tile steps
+// to arrive instead of one (verify batch -2 to -4%, prefill chunk -2%, BF16
+// -1%); a third tile measured no faster for FP8 rows and spills for BF16.
 template <int KV, int NV>
-constexpr int ws_depth() { return 1; }
+constexpr int ws_depth() { return 2; }
 
 // Waves that stage nothing (the score waves of the 12-wave form).
 struct NoStage {
@@ -735,8 +735,8 @@ struct NoStage {
 // fetched and tile 0 staged; iteration j = 0, 1, ... (at least through ntile,
 // in whole groups of three) calls work(j, ntile, P) (P = j % 3 at compile
 // time; work contains no barrier and does no role work past ntile), stages
-// tile j+1 into K buffer (j+1) % 3, fetches tile j+1+kD and waits at the
-// barrier.  Every thread stages, after its role work: with the staging
+// tile j+1 (held in register set (j+1) % kD) into K buffer (j+1) % 3,
+// fetches tile j+1+kD into that set and waits at the barrier.  Every thread stages, after its role work: with the staging
 // spread between the score waves' MFMAs, or done by the score waves alone,
 // the kernel measured slower.  Loads and stores run unconditionally (row
 // indices clamped to the chunk's last tile): past the last tile they refill
@@ -767,18 +767,28 @@ __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, in
     // Whole groups of three iterations, every one staging and fetching: the
     // fetches then form one straight-line stream whose in-order completion
     // counts the compiler can track (a conditional iteration makes it wait
-    // for every load in flight).  work() skips iterations past ntile.
-    for (int j0 = 0; j0 <= ntile; j0 += 3) {
+    // for every load in flight).  work() skips iterations past ntile.  The
+    // loop body holds two groups so that the register set of every
+    // iteration is known at compile time (kD divides six); an odd last group
+    // runs after the loop (an exit between the two groups spilled).
+    static_assert(6 % kD == 0, "register sets cycle within two groups of three");
+    auto group = [&](int j0, auto H) {
       dsa::static_for<3>([&](auto P) {
         constexpr int p = decltype(P)::value;
         const int j = j0 + p;
-        constexpr int si = (p + 1) % kD;
+        constexpr int si = (3 * decltype(H)::value + p + 1) % kD;
         work(j, ntile, P);
         st[si].store(sm.k[(p + 1) % 3], 0, sid);
         st[si].load(a.latent, tile_rows(j + 1 + kD), sid);
         __syncthreads();
       });
+    };
+    const int ngroups = ntile / 3 + 1;
+    for (int j0 = 0; j0 < 3 * (ngroups & ~1); j0 += 6) {
+      group(j0, std::integral_constant<int, 0>{});
+      group(j0 + 3, std::integral_constant<int, 1>{});
     }
+    if (ngroups & 1) group(3 * (ngroups - 1), std::integral_constant<int, 0>{});
   }
 }
 
