@@ -711,6 +711,7 @@ struct SmemWS {
   uint16_t k[3][kTileWS * kKStride];          // bf16 K tiles (ring of three)
   uint16_t p[2][DSA_HEADS * kPStrideWS];      // P of a tile in the PV operand's row order
   float alpha[2][DSA_HEADS];                  // O *= alpha before PV of that tile
+  uint32_t resc[2][4];                        // score wave w: a head of its tile moved its max
   int32_t rows[kRowChunk];
   float bias[kRowChunk];                      // 0 for a valid row, -inf for a masked one
   float fin_l[DSA_HEADS];
@@ -899,6 +900,10 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
             u32x4{pk[0], pk[1], pk[2], pk[3]};
         l_run += dsa::rows4_sum(psum);
         if (g == 0) sm.alpha[j & 1][head] = alpha;
+        // one word per wave for the value waves: does PV of this tile start
+        // with a rescale of O
+        const bool any_resc = __any(alpha != 1.f);
+        if (g == 0 && c == 0) sm.resc[j & 1][wave] = any_resc;
       }
     });
     if (g == 0) {
@@ -916,33 +921,39 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // V transpose read: rows 4g + c/4 (+16), columns kVCols*q + 16nb: logical
-    // chunk x = (kVCols/8)q + 2nb + (c%4)/2; bit 3 of the even chunk (the same
-    // for the whole wave) selects the lane base
+    // chunk x = (kVCols/8)q + 2nb + (c%4)/2; bit 3 of the even chunk selects
+    // the lane base, and as kVCols/8 is a multiple of 8 it flips with nb at
+    // compile time relative to nb = 0.  The lane offsets are computed once;
+    // each tile takes laundered copies, so the compiler cannot derive and
+    // hold per-ring-slot addresses from them (that spilled).
+    static_assert((kVCols / 8) % 8 == 0, "V lane base depends on q and nb only");
+    int v_even, v_odd, p_off;
+    {
+      const int ln = dsa::fresh_lane();
+      const int g = ln >> 4, c = ln & 15;
+      const int vrow = (4 * g + (c >> 2)) * kKStride + kVCols * q + 4 * (c & 1);
+      const int vlane0 = vrow + 8 * ((c & 3) >> 1);
+      const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
+      const bool hi0 = (((kVCols / 8) * q) >> 3) & 1;
+      v_even = hi0 ? vlane1 : vlane0;
+      v_odd = hi0 ? vlane0 : vlane1;
+      p_off = c * kPStrideWS + 8 * (g ^ p_swz(c));
+    }
     ws_pipeline<KV, NV, ValueStage>(a, sm, t, req, pos, c0, c1, wave, sid,
                                     [&](int j, int ntile, auto P) {
       constexpr int p = decltype(P)::value;
       if (j >= 1 && j <= ntile) {
         const int jp = j - 1;   // PV of the previous tile, in K buffer (p + 2) % 3
-        // per-lane LDS offsets computed each tile from a fresh lane index (a
-        // few VALU ops) instead of held for all three ring slots through the
-        // loop, where they spilled
-        const int ln = dsa::fresh_lane();
-        const int g = ln >> 4, c = ln & 15;
-        const int vrow = (4 * g + (c >> 2)) * kKStride + kVCols * q + 4 * (c & 1);
-        const int vlane0 = vrow + 8 * ((c & 3) >> 1);
-        const int vlane1 = vrow + 8 * (((c & 3) >> 1) ^ 1);
+        int ve = v_even, vo = v_odd, po = p_off;
+        asm volatile("" : "+v"(ve), "+v"(vo), "+v"(po));
         // O *= alpha of the heads this lane holds (rows 4g + jj of each head
-        // block); the factors are read again in the rare rescale branch rather
-        // than held in registers through it
-        const float* alp = sm.alpha[jp & 1] + 4 * g;
-        bool rescale = false;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          const f32x4 al = *reinterpret_cast<const f32x4*>(alp + 16 * hb);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[jj] != 1.f;
-        }
-        if (__any(rescale)) {
+        // block), only in the rare tiles where some score wave moved a head's
+        // reference: one LDS word per score wave says so, instead of every
+        // lane testing its 16 factors (that test's VALU work, on the SIMDs
+        // the score waves share, cost 4-5%)
+        const u32x4 rf = *reinterpret_cast<const u32x4*>(sm.resc[jp & 1]);
+        if (__builtin_amdgcn_readfirstlane(rf[0] | rf[1] | rf[2] | rf[3]) != 0) {
+          const float* alp = sm.alpha[jp & 1] + 4 * (dsa::fresh_lane() >> 4);
 #pragma unroll
           for (int hb = 0; hb < 4; ++hb) {
             const f32x4 al = *reinterpret_cast<const f32x4*>(alp + 16 * hb);
@@ -956,13 +967,12 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
         u32x4 pa[4];
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
-          pa[hb] = *reinterpret_cast<const u32x4*>(pb + (16 * hb + c) * kPStrideWS + 8 * (g ^ p_swz(c)));
+          pa[hb] = *reinterpret_cast<const u32x4*>(pb + 16 * hb * kPStrideWS + po);
         // V fragments read one column block ahead; one staging step of the
         // next tile after each block's four MFMAs
         const uint16_t* vt = sm.k[(p + 2) % 3];
         auto vread = [&](int nb) {
-          const int x = (kVCols / 8) * q + 2 * nb;
-          const uint16_t* vp = vt + ((x >> 3) & 1 ? vlane1 : vlane0) + 16 * nb;
+          const uint16_t* vp = vt + (((2 * nb) >> 3) & 1 ? vo : ve) + 16 * nb;
           const u32x2 lo2 = lds_read_tr16(vp);
           const u32x2 hi2 = lds_read_tr16(vp + 16 * kKStride);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
