@@ -1062,6 +1062,7 @@ struct SmemQ8 {
   uint16_t v[3][kTileQ8 * kVStrideQ8];         // dequantized latent (V), bf16
   uint16_t p[2][DSA_HEADS * kPStrideWS];       // P in the PV operand's row order
   float alpha[2][DSA_HEADS];
+  uint32_t resc[2][2];                        // score wave w: a head of its tile moved its max
   int32_t rows[kRowChunkQ8];
   float bias[kRowChunkQ8];
   float fin_l[DSA_HEADS];
@@ -1226,21 +1227,18 @@ __device__ __forceinline__ void q8_value(const PartialArgs& a, SmemQ8& sm, int t
     constexpr int p = decltype(P)::value;
     if (j >= 1 && j <= ntile) {
       const int jp = j - 1;
-      f32x4 al[4];
-      bool rescale = false;
+      // O *= alpha only in the rare tiles where a score wave moved a head's
+      // reference (one word per score wave)
+      const u32x2 rf = *reinterpret_cast<const u32x2*>(sm.resc[jp & 1]);
+      if (__builtin_amdgcn_readfirstlane(rf[0] | rf[1]) != 0) {
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        al[hb] = *reinterpret_cast<const f32x4*>(sm.alpha[jp & 1] + 16 * hb + 4 * g);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) rescale = rescale || al[hb][jj] != 1.f;
-      }
-      if (__any(rescale)) {
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
+        for (int hb = 0; hb < 4; ++hb) {
+          const f32x4 al = *reinterpret_cast<const f32x4*>(sm.alpha[jp & 1] + 16 * hb + 4 * g);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[hb][jj];
+            for (int jj = 0; jj < 4; ++jj) o[hb][nb][jj] *= al[jj];
+        }
       }
       const uint16_t* pb = sm.p[jp & 1];
       u32x4 pa[4];
@@ -1360,6 +1358,10 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
             u32x4{dsa::pack_bf16x2(pr[4], pr[5]), dsa::pack_bf16x2(pr[6], pr[7]),
                   dsa::pack_bf16x2(pr[12], pr[13]), dsa::pack_bf16x2(pr[14], pr[15])};
         if (h == 0) sm.alpha[j & 1][head] = alpha;
+        // one word per wave for the value waves: does PV of this tile start
+        // with a rescale of O
+        const bool any_resc = __any(alpha != 1.f);
+        if (lane == 0) sm.resc[j & 1][wave] = any_resc;
       }
     });
     const float l = halves_sum(l_run);
