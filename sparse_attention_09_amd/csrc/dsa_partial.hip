@@ -829,7 +829,9 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
 #pragma unroll
       for (int ks = 0; ks < kQS; ++ks) qf[ks] = qsrc[ks * 4 + g];
     }
-    float m_run = kNegInf, l_run = 0.f;
+    // running max of the head and this lane's share of its sum (rows 4g..+4
+    // of every block), summed over the lanes once at the end
+    float m_run = kNegInf, l_lane = 0.f;
     // K operand: rows 16mb + c, dims 32ks + 8g = logical chunk 4ks + g, physical
     // 4ks + (g ^ bit1(ks))
     const int klane0 = c * kKStride + 8 * g;
@@ -875,7 +877,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
         float alpha = 1.f;
         if (tmax > m_run + kRescaleThreshold) {
           if (m_run != kNegInf) alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-          l_run *= alpha;
+          l_lane *= alpha;
           m_run = tmax;
         }
         // masked rows: -inf * scale - m = -inf, exp2 gives 0; while no row has
@@ -883,7 +885,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
         const float neg_m = m_run == kNegInf ? 0.f : -m_run;
         // rows 16mb + 4g + jj -> PV operand position 8g + 4mb + jj: this lane's
         // eight values are logical chunk g of the head's P row
-        float psum = 0.f;
+        float psum = l_lane;
         uint32_t pk[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -898,7 +900,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
         }
         *reinterpret_cast<u32x4*>(sm.p[j & 1] + head * kPStrideWS + 8 * (g ^ p_swz(c))) =
             u32x4{pk[0], pk[1], pk[2], pk[3]};
-        l_run += dsa::rows4_sum(psum);
+        l_lane = psum;
         if (g == 0) sm.alpha[j & 1][head] = alpha;
         // one word per wave for the value waves: does PV of this tile start
         // with a rescale of O
@@ -906,6 +908,7 @@ __global__ __launch_bounds__((4 + NV) * 64) void partial_ws_kernel(PartialArgs a
         if (g == 0 && c == 0) sm.resc[j & 1][wave] = any_resc;
       }
     });
+    const float l_run = dsa::rows4_sum(l_lane);
     if (g == 0) {
       sm.fin_l[head] = l_run;
       put_lse<kFinal>(a, ts, head, l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : kNegInf);
