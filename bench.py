@@ -184,8 +184,8 @@ def cpu_baseline(wl, budget_s=15.0, max_tokens=512):
 # select, fallback.
 KERNEL_PATTERNS = [
     ("dcp_merge", r"dcp_merge_kernel"),
-    ("index_scores", r"index_kernel(ILi0E|<0>)"), ("index_sample", r"index_kernel(ILi1E|<1>)"),
-    ("index_emit", r"index_kernel(ILi2E|<2>)"), ("threshold", r"threshold_kernel"),
+    ("index_scores", r"index_kernel(ILi0E|<0[,>])"), ("index_sample", r"index_kernel(ILi1E|<1[,>])"),
+    ("index_emit", r"index_kernel(ILi2E|<2[,>])"), ("threshold", r"threshold_kernel"),
     ("select", r"select_kernel"), ("fallback", r"fallback_kernel"), ("topk", r"topk_kernel"),
     ("partial_q8", r"partial_q8_kernel"), ("quantize_q8", r"quantize_q8_kernel"),
     ("partial", r"partial"), ("combine", r"combine_kernel")]

@@ -48,8 +48,13 @@ using dsa::u32x4;
 // One work unit: request `req`, query block `qblock` (up to 8 tokens), chunk
 // `chunk` of pages.  Contains barriers; every thread of the workgroup runs it
 // with the same unit.  lds: two staging buffers of one page; cand_v/cand_p:
-// the emit pass's per-token candidate rows.
-template <int MODE>
+// the emit pass's per-token candidate rows.  kStream: the keys are read
+// with non-temporal loads, for batches that read each key once (caching
+// them only evicts what is reused, such as the emit pass's candidate lists:
+// verify batch selection -5%; where keys are read again, by the query blocks
+// of a prefill chunk or by requests sharing a prefix, cached loads are
+// 19-24% faster).
+template <int MODE, bool kStream>
 __device__ __forceinline__ void index_unit(
     const uint16_t* __restrict__ keys, int num_pages, const int32_t* __restrict__ page_table,
     int pt_stride, const int32_t* __restrict__ q_offsets, const int32_t* __restrict__ tok_pos,
@@ -158,7 +163,10 @@ __device__ __forceinline__ void index_unit(
   auto load_page = [&](u32x4 (&pre)[4], int pg) {
     const u32x4* src = page_src(pg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = src[tid + kThreads * i];
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kStream) pre[i] = __builtin_nontemporal_load(src + tid + kThreads * i);
+      else pre[i] = src[tid + kThreads * i];
+    }
   };
   auto store_page = [&](const u32x4 (&pre)[4], int buf) {
 #pragma unroll
@@ -351,7 +359,7 @@ __device__ __forceinline__ void index_unit(
 // Workgroup = unit (chunk blockIdx.x, request blockIdx.y, query block
 // blockIdx.z).  (A persistent grid with static unit assignment measured
 // slower: it loses the dispatcher's balancing of uneven units.)
-template <int MODE>
+template <int MODE, bool kStream>
 __global__ __launch_bounds__(kThreads, 4) void index_kernel(
     const uint16_t* __restrict__ keys, int num_pages, const int32_t* __restrict__ page_table,
     int pt_stride, const int32_t* __restrict__ q_offsets, const int32_t* __restrict__ tok_pos,
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 4) void index_kernel(
   __shared__ uint16_t cand_p[MODE == kEmit ? kQB * kCandLds : 1];
   // scores and sample passes: the last computed page's scores, per parity
   __shared__ __attribute__((aligned(16))) float sst[MODE != kEmit ? 2 * kQB * DSA_PAGE_TOKENS : 4];
-  index_unit<MODE>(keys, num_pages, page_table, pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld,
+  index_unit<MODE, kStream>(keys, num_pages, page_table, pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld,
                    max_ctx, num_tokens, em, lds, cand_v, cand_p, sst, blockIdx.x, blockIdx.y,
                    blockIdx.z);
 }
@@ -395,9 +403,23 @@ dsa_status launch_index(int mode, const dsa_pool* pool, const int32_t* page_tabl
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, st, keys, pool->num_pages, page_table,
                        pt_stride, q_offsets, tok_pos, q_idx, w, scores, ld, max_ctx, num_tokens, e);
   };
-  if (mode == kScores) go(index_kernel<kScores>, none);
-  else if (mode == kSample) go(index_kernel<kSample>, none);
-  else go(index_kernel<kEmit>, *em);
+  // Keys are streamed (non-temporal loads) when each request has a single
+  // query block and the requests' pages could all be distinct (the pool holds
+  // at least as many pages as the requests span).  A pool smaller than that
+  // means pages shared across requests (a common prefix), whose keys every
+  // request reads again: cached loads (shared-prefix batch: streamed 24%
+  // slower).  Sharing inside a larger pool is not detected here; it costs
+  // time, never correctness.
+  const bool stream_keys = qblocks <= 1 && int64_t(num_reqs) * pages <= pool->num_pages;
+  if (stream_keys) {
+    if (mode == kScores) go(index_kernel<kScores, true>, none);
+    else if (mode == kSample) go(index_kernel<kSample, true>, none);
+    else go(index_kernel<kEmit, true>, *em);
+  } else {
+    if (mode == kScores) go(index_kernel<kScores, false>, none);
+    else if (mode == kSample) go(index_kernel<kSample, false>, none);
+    else go(index_kernel<kEmit, false>, *em);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DSA_ERR_HIP, std::string("indexer: launch failed: ") + hipGetErrorString(e));
   return ok();
