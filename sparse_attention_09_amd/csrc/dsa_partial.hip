@@ -23,10 +23,10 @@
 //     made.
 // Kernels:
 //   * tiles of 32 and 128 index columns (partial_ws_kernel): 12 waves (8 for
-//     BF16 rows) in a
-//     score role and a value role one 32-row tile apart, a running reference
-//     max that rescales O only when it grows by more than 2^8 (described at
-//     the kernel); a 128-column tile is four of its 32-row LDS steps;
+//     BF16 rows) in a score role and a value role one 32-row tile apart, a
+//     running reference max that rescales O only when it grows by more than
+//     2^8 (described at the kernel); a 128-column tile is four of its 32-row
+//     LDS steps;
 //   * tiles of 64 (partial_v2_kernel, split batches): 8 waves, 2 per SIMD,
 //     each owning 32 heads, with a softmax whose per-head reference is fixed
 //     once (described at the kernel);
@@ -737,11 +737,11 @@ struct NoStage {
 // in whole groups of three) calls work(j, ntile, P) (P = j % 3 at compile
 // time; work contains no barrier and does no role work past ntile), stages
 // tile j+1 (held in register set (j+1) % kD) into K buffer (j+1) % 3,
-// fetches tile j+1+kD into that set and waits at the barrier.  Every thread stages, after its role work: with the staging
-// spread between the score waves' MFMAs, or done by the score waves alone,
-// the kernel measured slower.  Loads and stores run unconditionally (row
-// indices clamped to the chunk's last tile): past the last tile they refill
-// a buffer nobody reads.
+// fetches tile j+1+kD into that set and waits at the barrier.  The staging
+// follows the role work (spread between the score waves' MFMAs, done by the
+// score waves alone, or done before PV, it measured slower or no faster).
+// Loads and stores run unconditionally (row indices clamped to the chunk's
+// last tile): past the last tile they refill a buffer nobody reads.
 template <int KV, int NV, class Stager, class Work>
 __device__ __forceinline__ void ws_pipeline(const PartialArgs& a, SmemWS& sm, int t, int req,
                                             int pos, int c0, int c1, int wave, int sid,
