@@ -702,10 +702,18 @@ constexpr int kWSKLook = 2;                 // k-steps ahead the score waves rea
 constexpr int kPStrideWS = kTileWS;         // bf16 per head in a P buffer (64 bytes)
 
 // 16-byte chunk of a P row: logical chunk g (PV operand positions 8g..8g+7)
-// of head h sits at g ^ p_swz(h).  With this XOR the score waves' 16-byte
-// writes (8 lanes on 8 heads) and the value waves' 16-byte operand reads (16
-// heads x 4 chunks) are both free of bank conflicts.
-__device__ __forceinline__ int p_swz(int h) { return (((h >> 1) ^ (h >> 3)) & 1) | (((h >> 2) & 1) << 1); }
+// of head h sits at g ^ p_swz(h), p_swz(h) = bits 1-2 of h.  A 64-lane
+// 16-byte LDS read is served in four passes of 16 lanes: lanes 0-31 and
+// 32-63 apart, and within a half the lanes whose bits 2, 3 and 4 have even
+// parity apart from those with odd parity (measured: a probe that makes two
+// lanes l and l^m hit the same banks conflicts exactly for m in {1-3, 12-15,
+// 20-27}).  With heads h = lane & 15 and chunk groups g = lane >> 4, every
+// pass then meets 16 distinct 16-byte slots of its 256 bytes, for the value
+// waves' operand reads and for the score waves' writes of the same layout
+// (8 consecutive lanes, or the passes above).  The previous XOR (bit 0 =
+// bit 1 ^ bit 3 of h, bit 1 = bit 2) gave every P read 2-way conflicts:
+// 8.4M conflict cycles per verify-batch launch, 9% of its LDS activity.
+__device__ __forceinline__ int p_swz(int h) { return (h >> 1) & 3; }
 
 struct SmemWS {
   uint16_t k[3][kTileWS * kKStride];          // bf16 K tiles (ring of three)
