@@ -1057,13 +1057,14 @@ constexpr int kQ8Groups = DSA_D_QK / 64;       // 9 scale groups = 9 MFMA k-step
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Raw-code tile: logical 16-byte chunk x of row r at physical chunk
-// x ^ bit4(r).  A score lane (row m = l%32, half h = l/32) reads logical
-// chunks 4g + h and 4g + 2 + h of group g; a 32-lane pass of a 16-byte read
-// (lanes 0..15 with 48..63, then 16..47) meets rows m and m + 16 of opposite
-// halves, which the flip puts in the same physical chunk, and with the odd
-// stride the 32 rows fall on 32 distinct bank slots.  Staging writes (8 lanes
-// on 8 consecutive chunks of a row) are conflict-free as well.
+// Raw-code tile: rows 37 16-byte chunks apart (odd).  A score lane (row
+// m = l%32, half h = l/32) reads chunks 4g + h and 4g + 2 + h of group g; a
+// 16-byte read is served in passes of 16 lanes of one half whose lane bits
+// 2-4 share a parity, so a pass holds one of rows m and m + 16 for each m
+// mod 16, and the odd stride puts those 16 rows on 16 distinct bank slots.
+// (A flip of the chunk by bit 4 of the row, made for a wrongly assumed pass
+// grouping, put two rows of every pass on the same banks.)  Staging writes
+// (8 lanes on 8 consecutive chunks of a row) are conflict-free as well.
 // V tile: logical bf16 chunk x (8 values) of row r at k_phys(x), rows 33
 // 32-byte units apart (odd), which keeps the transpose reads and the staging
 // writes conflict-free, as in the bf16 K tile.
@@ -1153,7 +1154,7 @@ struct Q8Stage {
       const bool okb = (ok >> i) & 1u;
       const u32x4 cd = okb ? code[i] : u32x4{0, 0, 0, 0};
       const float s = okb ? scale[i] : 0.f;
-      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) = cd;
+      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * c) = cd;
       // bf16 chunks 2c, 2c + 1 at k_phys(2c), k_phys(2c) ^ 1
       const u32x2 a0 = dq4_bf16(cd[0], s), a1 = dq4_bf16(cd[1], s);
       *reinterpret_cast<u32x4*>(v + r * kVStrideQ8 + 8 * k_phys(2 * c)) =
@@ -1166,8 +1167,7 @@ struct Q8Stage {
     if constexpr (kRope) {
       const int rr = tid - 256, r = rr >> 2, c = DSA_D_LATENT / 16 + (rr & 3);
       const bool okb = (ok >> NC) & 1u;
-      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * (c ^ ((r >> 4) & 1))) =
-          okb ? rcode : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(k8 + r * kK8Stride + 16 * c) = okb ? rcode : u32x4{0, 0, 0, 0};
       if ((rr & 3) == 0) sc8[r * 16 + 8] = okb ? uint8_t(__float_as_uint(rscale) >> 23) : 0;
     }
   }
@@ -1312,7 +1312,7 @@ __global__ __launch_bounds__(kThreadsV2) void partial_q8_kernel(PartialArgs a) {
                      *reinterpret_cast<const u32x4*>(qs + 64 * g + 32));
     }
     const float cq = a.q8_scale[int64_t(t) * DSA_HEADS + head] * a.scale_log2;
-    const int ka = n * kK8Stride + 16 * (h ^ ((n >> 4) & 1));
+    const int ka = n * kK8Stride + 16 * h;
     const int sw = p_swz(head & 15);
     float m_run = kNegInf, l_run = 0.f;
     q8_pipeline<Q8Stage<2, false, 3>>(a, sm, t, req, pos, tid, 512 + tid, [&](int j, int ntile, auto) {
