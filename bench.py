@@ -11,6 +11,7 @@ each, FP8 E4M3 latent KV (per-64 power-of-two scales) in 64-token pages, top-204
   python bench.py --summarize-stats KERNEL_STATS_CSV COMMAND...      (rocprofv3 summary text)
   python bench.py --summarize-pmc FETCH_CSV WRITE_CSV WORKLOAD CMD... (traffic JSON)
   python bench.py --summarize-mfma COUNTER_CSV WORKLOAD CMD...        (MFMA-use JSON)
+  python bench.py --summarize-lds COUNTER_CSV WORKLOAD CMD...         (LDS-use JSON)
 
 With no flags the line also carries the 32K-token prefill chunk (Partial
 against the bf16 MFMA peak, and the Q8 variant: FP8 query quantizer + Q8
@@ -620,7 +621,43 @@ def bench_shared_prefix(dsa, synth, dev, cus, flush, steps=7, warmup=10, rounds=
     return out
 
 
+def summarize_lds(csv_path: str, workload: str, commands: list) -> dict:
+    """LDS use of each path kernel from a rocprofv3 counter run with
+    SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE (cycles, summed over the CUs),
+    SQ_INSTS_LDS and SQ_WAIT_INST_LDS (wave quad-cycles waiting to issue an LDS
+    instruction): per launch (median over dispatches), and the share of
+    LDS-active cycles lost to bank conflicts."""
+    import csv
+    import statistics
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = _kernel_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = {"workload": workload, "commands": commands,
+           "counters": "SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_INSTS_LDS, SQ_WAIT_INST_LDS "
+                       "per launch (median over dispatches); conflict_frac = conflict / active cycles",
+           "kernels": {}}
+    for k, ds in per.items():
+        rows = list(ds.values())
+        e = {"dispatches": len(rows), "source_sha": source_sha(k)}
+        for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS"):
+            vals = [r[c] for r in rows if c in r]
+            if vals:
+                e[c] = int(statistics.median(vals))
+        if e.get("SQ_LDS_IDX_ACTIVE"):
+            e["conflict_frac"] = round(e.get("SQ_LDS_BANK_CONFLICT", 0) / e["SQ_LDS_IDX_ACTIVE"], 4)
+        out["kernels"][k] = e
+    return out
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-lds":
+        csv_path, workload = sys.argv[2:4]
+        print(json.dumps(summarize_lds(csv_path, workload, sys.argv[4:]), indent=1))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
         print(summarize_stats(sys.argv[2], " ".join(sys.argv[3:])), end="")
         return

@@ -88,3 +88,23 @@ def test_mfma_summary_from_counters(tmp_path):
     assert k["mfma_tflops_counted"] == 1280.0
     assert k["busy_cycles_frac"] == 0.25
     assert k["mfma_util"] == 0.25
+
+
+def test_lds_summary_from_counters(tmp_path):
+    """LDS use per launch from a counter CSV: medians over dispatches and the
+    share of LDS-active cycles spent in bank conflicts."""
+    csv = tmp_path / "c.csv"
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"
+    rows = [head]
+    name = '"void (anonymous namespace)::partial_q8_kernel(x)"'
+    for d, conf in ((1, 10.0), (2, 30.0), (3, 20.0)):
+        for c, v in (("SQ_LDS_BANK_CONFLICT", conf), ("SQ_LDS_IDX_ACTIVE", 200.0),
+                     ("SQ_INSTS_LDS", 50.0), ("SQ_WAIT_INST_LDS", 7.0)):
+            rows.append(f"{d},{name},{c},{v},1000,2000")
+    csv.write_text("\n".join(rows) + "\n")
+    out = bench.summarize_lds(str(csv), "w", ["cmd"])
+    k = out["kernels"]["partial_q8"]
+    assert k["dispatches"] == 3
+    assert k["SQ_LDS_BANK_CONFLICT"] == 20 and k["SQ_LDS_IDX_ACTIVE"] == 200
+    assert k["conflict_frac"] == 0.1
+
